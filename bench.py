@@ -1,0 +1,211 @@
+"""Benchmark of the batched CFM sampler on one MI355X.
+
+One bench step = one cfm_sample call: the whole hot path (timestep MLP and
+modulation set-up, S Euler steps of the DiT estimator over the CFG-expanded
+batch, guidance combine and Euler update) over one batch of synthetic input,
+with inputs resident in HBM. Default workload: the Mel DiT generator
+(22 layers, d=1024, 16 heads, FFN 2048, 100-channel latent, 1000 frames,
+8 requests x CFG = 16 rows, text condition 1000x512, 32 Euler steps, s=2).
+
+Prints ONE JSON line on stdout:
+  value            estimator evals/s = rows * S / t_sample
+  frames           latent frame-steps/s and generated frames/s
+  gemm_attn_frac   GEMM + attention FLOPs / their kernel time / 2.5 PFLOP/s (bf16 dense)
+  roofline         the dominant kernel class: algorithmic FLOPs (or bytes) per launch /
+                   its mean launch duration (HIP events on the launch stream)
+  cpu_baseline     the fp64 CPU oracle on a bounded sample of the same workload
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+PEAK_BF16 = 2.5e15      # MI355X dense bf16 MFMA, FLOP/s
+PEAK_HBM = 8.0e12       # MI355X HBM3E, B/s
+MFMA_CLASSES = ["gemm_qkv", "gemm_proj", "gemm_fc1", "gemm_fc2", "attention", "gemm_in", "gemm_out"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def work_model(s, lengths):
+    """Algorithmic work per launch of each kernel class (valid tokens only) and launches per sample."""
+    R, Tx, C, d, f, H = s.n_requests, s.n_frames, s.latent_dim, s.d_model, s.ffn_dim, s.n_heads
+    P = s.n_prefix if s.cond_mode == "prefix" else 0
+    nb, L, S = s.n_branches, s.n_layers, s.n_steps
+    Lv = np.minimum(np.asarray(lengths), Tx)
+    tok_v = nb * float(np.sum(Lv + P))                  # valid tokens over all rows
+    x_v = float(np.sum(Lv))                              # valid latent frames over all requests
+    attn = 4.0 * s.head_dim * H * nb * float(np.sum((Lv + P) ** 2))
+    w = {
+        "gemm_qkv": (2.0 * tok_v * 3 * d * d, L * S),
+        "gemm_proj": (2.0 * tok_v * d * d, L * S),
+        "gemm_fc1": (2.0 * tok_v * f * d, L * S),
+        "gemm_fc2": (2.0 * tok_v * d * f, L * S),
+        "attention": (attn, L * S),
+        "gemm_in": (2.0 * x_v * d * C, S),
+        "gemm_out": (2.0 * nb * x_v * C * d, S),
+        # bytes: LN reads h fp32, writes bf16 (valid tokens); CFG+Euler reads x, writes x, reads nb v
+        "adaln": (tok_v * d * (4 + 2), 2 * L * S + S),
+        "cfg_euler": (x_v * C * 4 * (2 + nb), S),
+    }
+    return w
+
+
+def cpu_baseline(s, W, I, max_workers: int):
+    from oracle import sampler as O
+    cores = max(1, min(O.host_cores(), max_workers, s.n_requests))
+    reqs = list(range(cores))
+    t0 = time.perf_counter()
+    O.sample(W, s, I["x0"], I["cond"], I["spk"], I["mask"], 1, s.guidance, requests=reqs, workers=cores)
+    t = time.perf_counter() - t0
+    evals = len(reqs) * s.n_branches * 1
+    return {"value": evals / t, "unit": "estimator evals/s", "cores": cores, "kind": "oracle",
+            "sample": f"{s.name}: {len(reqs)} requests x 1 Euler step = {evals} row-evaluations of "
+                      f"{s.seq_len} frames, fp64 numpy oracle, one process per request with 1 BLAS "
+                      f"thread; {t:.1f} s wall on {platform.processor() or platform.machine()}",
+            "seconds": t}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="mel_dit", choices=synth.WORKLOAD_ORDER)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-workers", type=int, default=16)
+    ap.add_argument("--no-kernel-timing", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the sampler shards by request "
+              f"with no communication during sampling, so a multi-GPU figure is not measured here.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    s = synth.workload(args.workload)
+    t0 = time.perf_counter()
+    W, I = synth.make_weights(s), synth.make_inputs(s)
+    log(f"[bench] {s.name}: inputs drawn in {time.perf_counter() - t0:.1f} s")
+    base = None
+    if not args.no_cpu_baseline:      # before any GPU work: the oracle forks worker processes
+        base = cpu_baseline(s, W, I, args.cpu_workers)
+        log(f"[bench] cpu baseline: {base['value']:.3f} evals/s ({base['sample']})")
+
+    import torch
+    import flow_matching_tts_amd as F
+    from tests.helpers import config_for
+
+    torch.cuda.set_device(0)
+    smp = F.Sampler(config_for(s), W)
+    x0 = torch.from_numpy(I["x0"]).cuda()
+    cond = torch.from_numpy(I["cond"]).cuda()
+    spk = None if I["spk"] is None else torch.from_numpy(I["spk"]).cuda()
+    mask = None if I["mask"] is None else torch.from_numpy(I["mask"]).cuda()
+    out = torch.empty_like(x0)
+    run = lambda: smp.sample(x0, cond, mask=mask, spk=spk, n_steps=s.n_steps, guidance=s.guidance, out=out)
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run()
+    torch.cuda.synchronize()
+    first_ms = (time.perf_counter() - t0) * 1e3
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    log(f"[bench] first call {first_ms:.1f} ms; warmup {args.warmup} done")
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    log(f"[bench] {args.steps} timed steps: {ms:.3f} ms per sampling call")
+
+    lengths = I["lengths"]
+    rows = s.n_rows
+    evals_s = rows * s.n_steps / (ms / 1e3)
+    valid_frames = float(np.sum(np.minimum(lengths, s.n_frames)))
+    model = work_model(s, lengths)
+
+    kernels = {}
+    if not args.no_kernel_timing:
+        # per-class kernel time: one instrumented call per class (events around each launch)
+        for cls, (work, launches) in model.items():
+            smp.profile_enable(cls, launches + 8)
+            run()
+            tot, n, dropped = smp.profile_read()
+            smp.profile_disable()
+            kernels[cls] = {"ms_per_sample": tot, "launches": n, "mean_us": 1e3 * tot / max(n, 1)}
+        dom = max((c for c in kernels), key=lambda c: kernels[c]["ms_per_sample"])
+        # the dominant class again, live over the timed steps
+        work, launches = model[dom]
+        smp.profile_enable(dom, launches * args.steps + 8)
+        for _ in range(args.steps):
+            run()
+        tot, n, dropped = smp.profile_read()
+        smp.profile_disable()
+        mean_s = tot / 1e3 / n
+        mfma = dom in MFMA_CLASSES
+        achieved = work / mean_s
+        peak = PEAK_BF16 if mfma else PEAK_HBM
+        roofline = {"kernel_class": dom, "bound": "mfma" if mfma else "hbm",
+                    "achieved": achieved / (1e12 if mfma else 1e9), "peak": peak / (1e12 if mfma else 1e9),
+                    "unit": "TFLOP/s" if mfma else "GB/s", "frac": achieved / peak, "traffic": None,
+                    "mean_launch_us": mean_s * 1e6, "launches": n,
+                    "work_per_launch": work}
+        mf = sum(model[c][0] * model[c][1] for c in MFMA_CLASSES)
+        mt = sum(kernels[c]["ms_per_sample"] for c in MFMA_CLASSES) / 1e3
+        gemm_attn_frac = mf / mt / PEAK_BF16
+        for c, k in kernels.items():
+            work_c, launches_c = model.get(c, (None, None))
+            if work_c is None or k["launches"] == 0:
+                continue
+            rate = work_c * k["launches"] / (k["ms_per_sample"] / 1e3)
+            k["rate"] = rate / (1e12 if c in MFMA_CLASSES else 1e9)
+            k["rate_unit"] = "TFLOP/s" if c in MFMA_CLASSES else "GB/s"
+            k["frac"] = rate / (PEAK_BF16 if c in MFMA_CLASSES else PEAK_HBM)
+    else:
+        roofline, gemm_attn_frac = None, None
+        mf = sum(model[c][0] * model[c][1] for c in MFMA_CLASSES)
+
+    res = {
+        "metric": "estimator evals/sec and latent frames/sec per step; % bf16 MFMA peak",
+        "value": evals_s,
+        "unit": "estimator evals/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if s.dtype == "bf16" else "f32", "data": "synthetic",
+        "config": {"workload": s.name, "requests": s.n_requests, "branches": s.n_branches, "rows": rows,
+                   "frames": s.n_frames, "layers": s.n_layers, "d_model": s.d_model,
+                   "heads": s.n_heads, "ffn": s.ffn_dim, "latent": s.latent_dim,
+                   "euler_steps": s.n_steps, "guidance": list(s.guidance)},
+        "latent_frame_steps_per_s": valid_frames * s.n_steps / (ms / 1e3),
+        "generated_frames_per_s": valid_frames / (ms / 1e3),
+        "gemm_attn_frac_bf16_peak": gemm_attn_frac,
+        "end_to_end_frac_bf16_peak": mf / (ms / 1e3) / PEAK_BF16,
+        "first_call_ms": first_ms,
+        "roofline": roofline,
+        "cpu_baseline": base,
+        "kernels": kernels,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

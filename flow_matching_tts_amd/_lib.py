@@ -1,0 +1,256 @@
+"""ctypes binding of libcfm_mi355x.so (the C ABI in include/cfm.h).
+
+Argument marshalling only: every step of the sampler runs in the library's
+HIP kernels. torch supplies device memory and the current stream. There is no
+fallback: if the library is missing or was not built, loading raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Dict, Mapping, Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcfm_mi355x.so")
+
+CFM_F32, CFM_BF16 = 0, 1
+CFM_COND_CHANNEL, CFM_COND_PREFIX = 0, 1
+STATUS = {0: "CFM_OK", 1: "CFM_E_NULL", 2: "CFM_E_SHAPE", 3: "CFM_E_CAPACITY", 4: "CFM_E_VALUE",
+          5: "CFM_E_UNSUPPORTED", 6: "CFM_E_WORKSPACE", 7: "CFM_E_HIP"}
+KERNEL_CLASSES = {"gemm_qkv": 0, "gemm_proj": 1, "gemm_fc1": 2, "gemm_fc2": 3, "attention": 4,
+                  "adaln": 5, "cfg_euler": 6, "gemm_in": 7, "gemm_out": 8, "hoisted": 9}
+
+EXPORTS = ["cfm_weights_bytes", "cfm_workspace_bytes", "cfm_weight_manifest", "cfm_create",
+           "cfm_sample", "cfm_destroy", "cfm_status_string", "cfm_last_error_detail",
+           "cfm_profile_enable", "cfm_profile_read", "cfm_profile_disable", "cfm_cfg_euler",
+           "cfm_gemm_bf16", "cfm_attention_bf16", "cfm_adaln"]
+
+
+class cfm_config(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in (
+        "n_layers", "d_model", "n_heads", "ffn_dim", "latent_dim", "cond_dim", "cond_mode",
+        "n_prefix", "spk_dim", "t_freq_dim", "n_branches", "dtype", "max_requests",
+        "max_frames", "max_steps")]
+
+
+class cfm_tensor_desc(C.Structure):
+    _fields_ = [("name", C.c_char * 48), ("row0", C.c_int64), ("col0", C.c_int64),
+                ("rows", C.c_int64), ("cols", C.c_int64), ("ld", C.c_int64),
+                ("offset", C.c_int64), ("dtype", C.c_int32), ("reserved", C.c_int32)]
+
+
+class CfmError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+        self.status = status
+        self.detail = detail
+
+
+_lib = None
+
+
+def load() -> C.CDLL:
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m flow_matching_tts_amd.build`")
+    lib = C.CDLL(LIB_PATH)
+    vp, i32, f32p = C.c_void_p, C.c_int, C.POINTER(C.c_float)
+    cfgp = C.POINTER(cfm_config)
+    lib.cfm_weights_bytes.argtypes = [cfgp]
+    lib.cfm_weights_bytes.restype = C.c_size_t
+    lib.cfm_workspace_bytes.argtypes = [cfgp]
+    lib.cfm_workspace_bytes.restype = C.c_size_t
+    lib.cfm_weight_manifest.argtypes = [cfgp, C.POINTER(cfm_tensor_desc), i32]
+    lib.cfm_weight_manifest.restype = i32
+    lib.cfm_create.argtypes = [cfgp, vp, vp, C.c_size_t, C.POINTER(vp)]
+    lib.cfm_create.restype = i32
+    lib.cfm_sample.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, f32p, vp, vp]
+    lib.cfm_sample.restype = i32
+    lib.cfm_destroy.argtypes = [vp]
+    lib.cfm_destroy.restype = None
+    lib.cfm_status_string.argtypes = [i32]
+    lib.cfm_status_string.restype = C.c_char_p
+    lib.cfm_last_error_detail.argtypes = []
+    lib.cfm_last_error_detail.restype = C.c_char_p
+    lib.cfm_profile_enable.argtypes = [vp, i32, i32]
+    lib.cfm_profile_enable.restype = i32
+    lib.cfm_profile_read.argtypes = [vp, C.POINTER(C.c_double), C.POINTER(i32), C.POINTER(i32)]
+    lib.cfm_profile_read.restype = i32
+    lib.cfm_profile_disable.argtypes = [vp]
+    lib.cfm_profile_disable.restype = i32
+    lib.cfm_cfg_euler.argtypes = [vp, f32p, i32, C.c_float, vp, i32, i32, i32, vp, vp]
+    lib.cfm_cfg_euler.restype = i32
+    lib.cfm_gemm_bf16.argtypes = [vp, i32, i32, vp, i32, vp, i32, i32, i32, i32, vp, vp, i32, vp]
+    lib.cfm_gemm_bf16.restype = i32
+    lib.cfm_attention_bf16.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp]
+    lib.cfm_attention_bf16.restype = i32
+    lib.cfm_adaln.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp]
+    lib.cfm_adaln.restype = i32
+    _lib = lib
+    return lib
+
+
+def check(status: int) -> None:
+    if status != 0:
+        detail = load().cfm_last_error_detail().decode()
+        raise CfmError(status, detail)
+
+
+def make_config(*, n_layers, d_model, n_heads, ffn_dim, latent_dim, cond_dim, cond_mode,
+                n_prefix, spk_dim, n_branches, dtype, max_requests, max_frames, max_steps,
+                t_freq_dim=256) -> cfm_config:
+    cm = {"channel": CFM_COND_CHANNEL, "prefix": CFM_COND_PREFIX}.get(cond_mode, cond_mode)
+    dt = {"f32": CFM_F32, "bf16": CFM_BF16}.get(dtype, dtype)
+    return cfm_config(n_layers, d_model, n_heads, ffn_dim, latent_dim, cond_dim, cm, n_prefix,
+                      spk_dim, t_freq_dim, n_branches, dt, max_requests, max_frames, max_steps)
+
+
+def weights_bytes(cfg: cfm_config) -> int:
+    return int(load().cfm_weights_bytes(C.byref(cfg)))
+
+
+def workspace_bytes(cfg: cfm_config) -> int:
+    return int(load().cfm_workspace_bytes(C.byref(cfg)))
+
+
+def weight_manifest(cfg: cfm_config):
+    lib = load()
+    n = lib.cfm_weight_manifest(C.byref(cfg), None, 0)
+    if n < 0:
+        check(-n)
+    arr = (cfm_tensor_desc * n)()
+    check(0 if lib.cfm_weight_manifest(C.byref(cfg), arr, n) == n else 4)
+    return [dict(name=a.name.decode(), row0=a.row0, col0=a.col0, rows=a.rows, cols=a.cols,
+                 ld=a.ld, offset=a.offset, dtype=a.dtype) for a in arr]
+
+
+def pack_weights(cfg: cfm_config, weights: Mapping[str, np.ndarray]) -> np.ndarray:
+    """Host byte image of the flat weight buffer, laid out as the manifest says."""
+    import torch
+    buf = np.zeros(weights_bytes(cfg), dtype=np.uint8)
+    for e in weight_manifest(cfg):
+        src = np.asarray(weights[e["name"]], dtype=np.float32)
+        if src.ndim == 1:
+            src = src[None, :]
+        blk = src[e["row0"]:e["row0"] + e["rows"], e["col0"]:e["col0"] + e["cols"]]
+        if blk.shape != (e["rows"], e["cols"]):
+            raise ValueError(f"{e['name']}: shape {src.shape} does not cover slot {e}")
+        pad = np.zeros((e["rows"], e["ld"]), dtype=np.float32)
+        pad[:, :e["cols"]] = blk
+        if e["dtype"] == CFM_BF16:
+            raw = torch.from_numpy(pad).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint8)
+        else:
+            raw = pad.view(np.uint8)
+        raw = raw.reshape(-1)
+        buf[e["offset"]:e["offset"] + raw.size] = raw
+    return buf
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+class Sampler:
+    """Owns the device weight buffer and workspace of one context (torch tensors)."""
+
+    def __init__(self, cfg: cfm_config, weights: Mapping[str, np.ndarray], device: str = "cuda"):
+        import torch
+        lib = load()
+        self.cfg = cfg
+        host = pack_weights(cfg, weights)
+        self.weights = torch.from_numpy(host).to(device)
+        self.workspace = torch.empty(max(workspace_bytes(cfg), 256), dtype=torch.uint8, device=device)
+        ctx = C.c_void_p()
+        check(lib.cfm_create(C.byref(cfg), self.weights.data_ptr(), self.workspace.data_ptr(),
+                             self.workspace.numel(), C.byref(ctx)))
+        self._ctx = ctx
+
+    @property
+    def ctx(self):
+        return self._ctx
+
+    def close(self):
+        if getattr(self, "_ctx", None) is not None and self._ctx.value:
+            load().cfm_destroy(self._ctx)
+            self._ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def sample(self, x0, cond, *, mask=None, spk=None, n_steps: int, guidance: Sequence[float] = (),
+               out=None, stream=None):
+        """out[R, Tx, C] (fp32, device) after n_steps Euler steps; out may be x0 itself."""
+        import torch
+        R, Tx = int(x0.shape[0]), int(x0.shape[1])
+        for name, t, dt in (("x0", x0, torch.float32), ("cond", cond, torch.float32),
+                            ("spk", spk, torch.float32), ("mask", mask, torch.uint8),
+                            ("out", out, torch.float32)):
+            if t is not None and (t.dtype != dt or not t.is_contiguous() or not t.is_cuda):
+                raise ValueError(f"{name} must be a contiguous CUDA {dt} tensor")
+        if out is None:
+            out = torch.empty_like(x0)
+        g = (C.c_float * max(1, len(guidance)))(*[float(v) for v in guidance])
+        check(load().cfm_sample(self._ctx, _ptr(x0), _ptr(cond), _ptr(spk), _ptr(mask), R, Tx,
+                                int(n_steps), g, _ptr(out), _stream(stream)))
+        return out
+
+    def profile_enable(self, kernel_class: str, capacity: int):
+        check(load().cfm_profile_enable(self._ctx, KERNEL_CLASSES[kernel_class], int(capacity)))
+
+    def profile_read(self):
+        ms, n, dropped = C.c_double(), C.c_int(), C.c_int()
+        check(load().cfm_profile_read(self._ctx, C.byref(ms), C.byref(n), C.byref(dropped)))
+        return ms.value, n.value, dropped.value
+
+    def profile_disable(self):
+        check(load().cfm_profile_disable(self._ctx))
+
+
+# ---------------------------------------------------------------- single kernels
+
+def cfg_euler(v, w: Sequence[float], dt: float, x, mask=None, stream=None):
+    nb, R, Tx, Cc = (int(s) for s in v.shape)
+    ww = (C.c_float * nb)(*[float(a) for a in w])
+    check(load().cfm_cfg_euler(_ptr(v), ww, nb, float(dt), _ptr(mask), R, Tx, Cc, _ptr(x), _stream(stream)))
+    return x
+
+
+def gemm_bf16(A, W, bias=None, *, epilogue: int, out, gate=None, K: Optional[int] = None, stream=None):
+    """out = epilogue(A[:, :K] W[:, :K]^T + bias); A bf16 or fp32, W bf16 [N, ldw]."""
+    import torch
+    M, lda = int(A.shape[0]), int(A.shape[1])
+    N, ldw = int(W.shape[0]), int(W.shape[1])
+    K = lda if K is None else int(K)
+    a_f32 = 1 if A.dtype == torch.float32 else 0
+    check(load().cfm_gemm_bf16(_ptr(A), a_f32, lda, _ptr(W), ldw, _ptr(bias), M, N, K, int(epilogue),
+                               _ptr(gate), _ptr(out), int(out.shape[1]), _stream(stream)))
+    return out
+
+
+def attention_bf16(qkv, kv_len, o, *, n_heads: int, key_mask=None, stream=None):
+    rows, T = int(qkv.shape[0]), int(qkv.shape[1])
+    check(load().cfm_attention_bf16(_ptr(qkv), _ptr(kv_len), _ptr(key_mask), rows, T, int(n_heads),
+                                    _ptr(o), _stream(stream)))
+    return o
+
+
+def adaln(h, shift, scale, y, stream=None):
+    import torch
+    M, d = int(h.shape[0]), int(h.shape[1])
+    check(load().cfm_adaln(_ptr(h), _ptr(shift), _ptr(scale), M, d, 1 if y.dtype == torch.bfloat16 else 0,
+                           _ptr(y), _stream(stream)))
+    return y

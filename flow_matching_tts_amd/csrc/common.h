@@ -1,0 +1,56 @@
+// Shared device helpers for the gfx950 kernels: bf16 packing, wave64
+// reductions, MFMA vector types and the row -> modulation-vector mapping.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cfm {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+
+__device__ __forceinline__ float gelu_erf(float x) {
+    // exact GELU: x * Phi(x) = x/2 (1 + erf(x / sqrt 2)), erf from the device math library
+    return 0.5f * x * (1.0f + erff(x * 0.70710678118654752440f));
+}
+
+__device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
+
+// Where a row's modulation vectors live. Rows are branch-major (row = b*R + r);
+// token m belongs to row m / tokens_per_row. Every row reads conditioning
+// vector 0 except the rows of branch `spk_branch`, whose condition carries the
+// request's speaker vector and reads vector 1 + r.
+struct RowMod {
+    const float* base;      // vector 0 of the current step, already offset to the chunk
+    long long cvec_stride;  // floats between consecutive conditioning vectors
+    int tokens_per_row;
+    int n_requests;
+    int spk_branch;         // -1: every row uses vector 0
+
+    __device__ __forceinline__ const float* at(long long m) const {
+        if (spk_branch < 0) return base;
+        int row = (int)(m / tokens_per_row);
+        int b = row / n_requests;
+        int r = row - b * n_requests;
+        return base + (b == spk_branch ? (long long)(1 + r) * cvec_stride : 0);
+    }
+};
+
+}  // namespace cfm

@@ -1,0 +1,78 @@
+// Launchers of the gfx950 kernels (host side), shared by the C-ABI runtime.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include "common.h"
+
+namespace cfm {
+
+// GEMM epilogues: what happens to acc[m, n] = sum_k A[m,k] W[n,k].
+enum Epi {
+    EPI_F32 = 0,       // out f32 [m, n] = acc + bias
+    EPI_ACT = 1,       // out act (bf16 on the MFMA path, f32 on the SIMT path) = acc + bias
+    EPI_GELU_ACT = 2,  // out act = GELU(acc + bias)
+    EPI_GATED = 3,     // out f32 [m, n] += gate(m)[n] * (acc + bias)
+    EPI_INPROJ = 4,    // input projection of latent token m = r*Tx + t into every branch row
+    EPI_VOUT = 5,      // velocity: out f32 [m, n] = frame valid ? acc + bias : 0
+};
+
+struct EpiParams {
+    const float* bias = nullptr;     // [N] or null
+    void* out = nullptr;
+    long long ldo = 0;               // row stride of out, elements
+    RowMod gate{};                   // EPI_GATED: gate vector of token m
+    // EPI_INPROJ: latent token m = r*Tx + t lands at token (b*R + r)*T + P + t
+    // of every branch b; branches b >= cond_branch0 add the condition
+    // projection cproj[m, n] (which already holds the bias), the others add bias.
+    int R = 0, Tx = 0, T = 0, P = 0, nb = 0, cond_branch0 = 1;
+    const float* cproj = nullptr;
+    // EPI_VOUT: m = row*Tx + t, request r = row % R, mask [R, Tx] or null
+    const uint8_t* mask = nullptr;
+};
+
+// bf16 MFMA GEMM, A bf16 or f32 (rounded to bf16 while staging), W bf16 [N, K].
+void launch_gemm_bf16(bool a_f32, int epi, const void* A, int lda, const bf16* W, int ldw,
+                      int M, int N, int K, const EpiParams& ep, hipStream_t s);
+// fp32 SIMT GEMM, A f32 (optionally SiLU on load), W f32 or bf16 [N, K]; EPI_ACT stores f32.
+void launch_gemm_simt(bool w_bf16, bool silu_a, int epi, const float* A, int lda, const void* W,
+                      int ldw, int M, int N, int K, const EpiParams& ep, hipStream_t s);
+
+struct AttnParams {
+    const void* qkv;          // [rows, T, 3d]
+    void* o;                  // [rows, T, d]
+    int rows, T, H, hd;
+    const int32_t* kv_len;    // per (row % kv_mod): keys >= kv_len are masked
+    int kv_mod;
+    const uint8_t* key_mask;  // [(row % kv_mod), Tm] for keys >= P, or null
+    int mask_stride;          // Tm
+    int P;                    // keys < P are always valid (condition prefix)
+};
+void launch_attention_bf16(const AttnParams& p, hipStream_t s);
+void launch_attention_f32(const AttnParams& p, hipStream_t s);
+
+// adaLN LayerNorm: output token o = row*Tout + t reads input token row*Tin + off + t.
+struct LnParams {
+    const float* h;
+    void* y;
+    int d;
+    long long n_out;          // output tokens
+    int Tin, Tout, off;
+    RowMod shift, scale;      // RowMod evaluated on the OUTPUT token index
+    int out_bf16;
+};
+void launch_adaln(const LnParams& p, hipStream_t s);
+
+void launch_cfg_euler(const float* v, int nb, float w0, float w1, float w2, const uint8_t* mask,
+                      int R, int Tx, int C, float* x, hipStream_t s);
+// temb [S, F] = sinusoidal embedding of t_k = k / S (phase in fp64)
+void launch_timestep_embedding(float* temb, int S, int F, hipStream_t s);
+// kv_len[r] = P + (index of last valid frame of request r) + 1
+void launch_kv_len(const uint8_t* mask, int R, int Tx, int P, int32_t* kv_len, hipStream_t s);
+// cvec[(k*nc + ci), :] = ct[k, :] + (spk ? (ci == 0 ? bs : spkproj[ci-1]) : 0)
+void launch_assemble_cvec(const float* ct, const float* bs, const float* spkproj, int S, int nc,
+                          int d, float* cvec, hipStream_t s);
+// prefix tokens of every branch row: h[(b*R + r)*T + p] = b >= cond_branch0 ? cproj[r*P + p] : bias
+void launch_prefix_init(const float* cproj, const float* bias, int R, int nb, int cond_branch0,
+                        int P, int T, int d, float* h, hipStream_t s);
+
+}  // namespace cfm

@@ -1,0 +1,626 @@
+// Host runtime behind include/cfm.h: argument validation, weight manifest,
+// workspace carve-up and the launch sequence of one sampling call.
+//
+// A call enqueues, on the caller's stream and with no host synchronisation:
+//   set-up (once per call): out <- x0; per-request key lengths; timestep
+//     embeddings of every step; timestep MLP; speaker projection; the adaLN
+//     modulation vectors of every step and layer; the projection of the
+//     condition features (constant over steps). VoiceHub's "Recommended
+//     optimization boundaries" asks to cache masks and conditioning outside the
+//     repeated estimator; this is that hoisting.
+//   per Euler step: input projection into every branch row, L DiT blocks
+//     (adaLN-LN, QKV GEMM, masked attention, out-proj GEMM + gated residual,
+//     adaLN-LN, FC1 GEMM + GELU, FC2 GEMM + gated residual), final adaLN-LN,
+//     output projection to the branch velocities, fused CFG combine + Euler.
+// The step loop never reads device memory back: the step size and guidance
+// weights are kernel arguments computed on the host (the vLLM-Omni blog's
+// "CFM/LocDiT decode-tail batching" section removes exactly such per-step
+// host syncs from its Euler loop).
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/cfm.h"
+#include "kernels.h"
+
+using namespace cfm;
+
+namespace {
+
+thread_local std::string g_detail;
+
+cfm_status fail(cfm_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+cfm_status fail(cfm_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_detail = buf;
+    return s;
+}
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+inline long long round8(long long v) { return (v + 7) / 8 * 8; }
+
+cfm_status check_config(const cfm_config* c) {
+    if (c == nullptr) return fail(CFM_E_NULL, "config is NULL");
+    if (c->n_layers < 0 || c->d_model <= 0 || c->n_heads <= 0 || c->ffn_dim <= 0 ||
+        c->latent_dim <= 0 || c->cond_dim < 0 || c->n_prefix < 0 || c->spk_dim < 0 ||
+        c->t_freq_dim <= 0 || c->max_requests < 0 || c->max_frames < 0 || c->max_steps < 0)
+        return fail(CFM_E_VALUE, "negative or zero size in config");
+    if (c->dtype != CFM_F32 && c->dtype != CFM_BF16) return fail(CFM_E_UNSUPPORTED, "dtype %d", c->dtype);
+    if (c->cond_mode != CFM_COND_CHANNEL && c->cond_mode != CFM_COND_PREFIX)
+        return fail(CFM_E_UNSUPPORTED, "cond_mode %d", c->cond_mode);
+    if (c->n_branches < 1 || c->n_branches > 3) return fail(CFM_E_UNSUPPORTED, "n_branches %d", c->n_branches);
+    if (c->d_model % c->n_heads) return fail(CFM_E_UNSUPPORTED, "d_model %% n_heads != 0");
+    const int hd = c->d_model / c->n_heads;
+    if (c->d_model % 8 || c->ffn_dim % 8) return fail(CFM_E_UNSUPPORTED, "d_model and ffn_dim must be multiples of 8");
+    if (c->d_model > 4096) return fail(CFM_E_UNSUPPORTED, "d_model above 4096");
+    if (c->latent_dim % 4 || c->cond_dim % 4) return fail(CFM_E_UNSUPPORTED, "latent_dim and cond_dim must be multiples of 4");
+    if (c->t_freq_dim % 8) return fail(CFM_E_UNSUPPORTED, "t_freq_dim must be a multiple of 8");
+    if (c->spk_dim % 4) return fail(CFM_E_UNSUPPORTED, "spk_dim must be a multiple of 4");
+    if (c->dtype == CFM_BF16 && hd != 64) return fail(CFM_E_UNSUPPORTED, "bf16 path needs head_dim 64 (got %d)", hd);
+    if (c->dtype == CFM_F32 && (hd % 4 || hd > 64)) return fail(CFM_E_UNSUPPORTED, "fp32 path needs head_dim %% 4 == 0 and <= 64");
+    if (c->cond_mode == CFM_COND_PREFIX) {
+        if (c->n_prefix <= 0) return fail(CFM_E_UNSUPPORTED, "prefix mode needs n_prefix > 0");
+        if (c->cond_dim != c->latent_dim) return fail(CFM_E_UNSUPPORTED, "prefix mode needs cond_dim == latent_dim");
+    } else {
+        if (c->n_prefix != 0) return fail(CFM_E_UNSUPPORTED, "channel mode needs n_prefix == 0");
+        if (c->cond_dim <= 0) return fail(CFM_E_UNSUPPORTED, "channel mode needs cond_dim > 0");
+    }
+    return CFM_OK;
+}
+
+struct Slot {
+    long long off = -1;   // bytes
+    int ld = 0;           // elements
+};
+
+struct Manifest {
+    std::vector<cfm_tensor_desc> d;
+    size_t bytes = 0;
+};
+
+// Builds the slot list; the same function fixes the offsets for the binding
+// (through cfm_weight_manifest) and for the runtime (through find()).
+Manifest build_manifest(const cfm_config& c) {
+    Manifest m;
+    const int mat_dt = c.dtype;
+    const size_t mat_es = c.dtype == CFM_BF16 ? 2 : 4;
+    size_t off = 0;
+    auto add = [&](const char* name, long long row0, long long col0, long long rows, long long cols,
+                   bool vec, bool packed) {
+        cfm_tensor_desc t;
+        std::memset(&t, 0, sizeof t);
+        std::snprintf(t.name, sizeof t.name, "%s", name);
+        t.row0 = row0; t.col0 = col0; t.rows = rows; t.cols = cols;
+        t.dtype = vec ? CFM_F32 : mat_dt;
+        t.ld = vec ? cols : round8(cols);
+        const size_t es = vec ? 4 : mat_es;
+        if (!packed) off = align_up(off, 256);
+        t.offset = (long long)off;
+        off += (size_t)rows * t.ld * es;
+        m.d.push_back(t);
+    };
+    const long long d = c.d_model, f = c.ffn_dim, C = c.latent_dim;
+    char nm[64];
+    add("t_embed.fc1.weight", 0, 0, d, c.t_freq_dim, false, false);
+    add("t_embed.fc1.bias", 0, 0, 1, d, true, false);
+    add("t_embed.fc2.weight", 0, 0, d, d, false, false);
+    add("t_embed.fc2.bias", 0, 0, 1, d, true, false);
+    if (c.spk_dim > 0) {
+        add("spk_proj.weight", 0, 0, d, c.spk_dim, false, false);
+        add("spk_proj.bias", 0, 0, 1, d, true, false);
+    }
+    add("in_proj.weight", 0, 0, d, C, false, false);
+    if (c.cond_mode == CFM_COND_CHANNEL) add("in_proj.weight", 0, C, d, c.cond_dim, false, false);
+    add("in_proj.bias", 0, 0, 1, d, true, false);
+    // all adaLN projections back to back: one GEMM produces every layer's modulation
+    for (int l = 0; l < c.n_layers; ++l) {
+        std::snprintf(nm, sizeof nm, "blocks.%d.ada.weight", l);
+        add(nm, 0, 0, 6 * d, d, false, l > 0);
+    }
+    add("final.ada.weight", 0, 0, 2 * d, d, false, c.n_layers > 0);
+    for (int l = 0; l < c.n_layers; ++l) {
+        std::snprintf(nm, sizeof nm, "blocks.%d.ada.bias", l);
+        add(nm, 0, 0, 1, 6 * d, true, l > 0);
+    }
+    add("final.ada.bias", 0, 0, 1, 2 * d, true, c.n_layers > 0);
+    for (int l = 0; l < c.n_layers; ++l) {
+        const char* parts[4] = {"qkv", "proj", "fc1", "fc2"};
+        const long long rows[4] = {3 * d, d, f, d};
+        const long long cols[4] = {d, d, d, f};
+        for (int i = 0; i < 4; ++i) {
+            std::snprintf(nm, sizeof nm, "blocks.%d.%s.weight", l, parts[i]);
+            add(nm, 0, 0, rows[i], cols[i], false, false);
+            std::snprintf(nm, sizeof nm, "blocks.%d.%s.bias", l, parts[i]);
+            add(nm, 0, 0, 1, rows[i], true, false);
+        }
+    }
+    add("final.out.weight", 0, 0, C, d, false, false);
+    add("final.out.bias", 0, 0, 1, C, true, false);
+    m.bytes = align_up(off, 256);
+    return m;
+}
+
+Slot find(const Manifest& m, const char* name, long long col0 = 0) {
+    for (const auto& t : m.d)
+        if (std::strcmp(t.name, name) == 0 && t.col0 == col0) return Slot{t.offset, (int)t.ld};
+    return Slot{};
+}
+
+struct Layout {   // workspace regions, byte offsets
+    size_t h, act, big, v, cproj, temb, tpre, ct, spkproj, cvec, mod, kvlen, total;
+};
+
+Layout plan_workspace(const cfm_config& c) {
+    const size_t es = c.dtype == CFM_BF16 ? 2 : 4;
+    const size_t Rm = c.max_requests, Tx = c.max_frames, S = c.max_steps;
+    const size_t P = c.cond_mode == CFM_COND_PREFIX ? c.n_prefix : 0;
+    const size_t T = Tx + P, N = (size_t)c.n_branches * Rm, d = c.d_model;
+    const size_t Tc = c.cond_mode == CFM_COND_PREFIX ? P : Tx;
+    const size_t nc = 1 + (c.spk_dim > 0 ? Rm : 0);
+    const size_t ML = (6 * (size_t)c.n_layers + 2) * d;
+    const size_t wide = std::max<size_t>(3 * d, c.ffn_dim);
+    Layout L;
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, 256); return o; };
+    L.h = take(N * T * d * 4);
+    L.act = take(N * T * d * es);
+    L.big = take(N * T * wide * es);
+    L.v = take(N * Tx * c.latent_dim * 4);
+    L.cproj = take(Rm * Tc * d * 4);
+    L.temb = take(S * c.t_freq_dim * 4);
+    L.tpre = take(S * d * 4);
+    L.ct = take(S * d * 4);
+    L.spkproj = take(c.spk_dim > 0 ? Rm * d * 4 : 0);
+    L.cvec = take(S * nc * d * 4);
+    L.mod = take(S * nc * ML * 4);
+    L.kvlen = take(Rm * 4);
+    L.total = off;
+    return L;
+}
+
+}  // namespace
+
+struct cfm_ctx {
+    cfm_config cfg;
+    const char* w = nullptr;
+    char* ws = nullptr;
+    size_t ws_bytes = 0;
+    Manifest man;
+    Layout lay;
+    Slot t1w, t1b, t2w, t2b, spkw, spkb, inxw, incw, inb, adaw, adab, outw, outb;
+    struct LayerW { Slot qkvw, qkvb, projw, projb, fc1w, fc1b, fc2w, fc2b; };
+    std::vector<LayerW> layers;
+    // kernel timing
+    int prof_class = -1, prof_cap = 0, prof_used = 0, prof_dropped = 0;
+    std::vector<hipEvent_t> ev0, ev1;
+};
+
+namespace {
+
+template <typename T> const T* wp(const cfm_ctx* c, Slot s) { return (const T*)(c->w + s.off); }
+template <typename T> T* wsp(const cfm_ctx* c, size_t off) { return (T*)(c->ws + off); }
+
+// Runs `fn` (one kernel launch) bracketed by timing events when its class is profiled.
+template <typename F>
+void timed(cfm_ctx* c, int cls, hipStream_t s, F&& fn) {
+    if (cls == c->prof_class && c->prof_class >= 0) {
+        if (c->prof_used < c->prof_cap) {
+            (void)hipEventRecord(c->ev0[c->prof_used], s);
+            fn();
+            (void)hipEventRecord(c->ev1[c->prof_used], s);
+            ++c->prof_used;
+            return;
+        }
+        ++c->prof_dropped;
+    }
+    fn();
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* cfm_status_string(cfm_status s) {
+    switch (s) {
+        case CFM_OK: return "ok";
+        case CFM_E_NULL: return "null pointer";
+        case CFM_E_SHAPE: return "bad shape or layout";
+        case CFM_E_CAPACITY: return "above create-time capacity";
+        case CFM_E_VALUE: return "bad value";
+        case CFM_E_UNSUPPORTED: return "unsupported configuration";
+        case CFM_E_WORKSPACE: return "workspace too small";
+        case CFM_E_HIP: return "HIP error";
+    }
+    return "unknown status";
+}
+
+const char* cfm_last_error_detail(void) { return g_detail.c_str(); }
+
+size_t cfm_weights_bytes(const cfm_config* cfg) {
+    if (check_config(cfg) != CFM_OK) return 0;
+    return build_manifest(*cfg).bytes;
+}
+
+size_t cfm_workspace_bytes(const cfm_config* cfg) {
+    if (check_config(cfg) != CFM_OK) return 0;
+    return plan_workspace(*cfg).total;
+}
+
+int cfm_weight_manifest(const cfm_config* cfg, cfm_tensor_desc* out, int cap) {
+    cfm_status st = check_config(cfg);
+    if (st != CFM_OK) return -(int)st;
+    if (cap > 0 && out == nullptr) return -(int)fail(CFM_E_NULL, "manifest output is NULL");
+    Manifest m = build_manifest(*cfg);
+    for (int i = 0; i < cap && i < (int)m.d.size(); ++i) out[i] = m.d[i];
+    return (int)m.d.size();
+}
+
+cfm_status cfm_create(const cfm_config* cfg, const void* weights, void* workspace,
+                      size_t workspace_bytes, cfm_ctx** out_ctx) {
+    if (out_ctx == nullptr) return fail(CFM_E_NULL, "out_ctx is NULL");
+    *out_ctx = nullptr;
+    cfm_status st = check_config(cfg);
+    if (st != CFM_OK) return st;
+    if (weights == nullptr) return fail(CFM_E_NULL, "weights is NULL");
+    Layout lay = plan_workspace(*cfg);
+    if (lay.total > 0 && workspace == nullptr) return fail(CFM_E_NULL, "workspace is NULL");
+    if (workspace_bytes < lay.total)
+        return fail(CFM_E_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, lay.total);
+    if (((uintptr_t)weights & 255) || ((uintptr_t)workspace & 255))
+        return fail(CFM_E_SHAPE, "weights and workspace must be 256-byte aligned");
+    cfm_ctx* c = new (std::nothrow) cfm_ctx;
+    if (c == nullptr) return fail(CFM_E_VALUE, "host allocation failed");
+    c->cfg = *cfg;
+    c->w = (const char*)weights;
+    c->ws = (char*)workspace;
+    c->ws_bytes = workspace_bytes;
+    c->man = build_manifest(*cfg);
+    c->lay = lay;
+    c->t1w = find(c->man, "t_embed.fc1.weight");
+    c->t1b = find(c->man, "t_embed.fc1.bias");
+    c->t2w = find(c->man, "t_embed.fc2.weight");
+    c->t2b = find(c->man, "t_embed.fc2.bias");
+    if (cfg->spk_dim > 0) {
+        c->spkw = find(c->man, "spk_proj.weight");
+        c->spkb = find(c->man, "spk_proj.bias");
+    }
+    c->inxw = find(c->man, "in_proj.weight", 0);
+    if (cfg->cond_mode == CFM_COND_CHANNEL) c->incw = find(c->man, "in_proj.weight", cfg->latent_dim);
+    c->inb = find(c->man, "in_proj.bias");
+    c->adaw = cfg->n_layers > 0 ? find(c->man, "blocks.0.ada.weight") : find(c->man, "final.ada.weight");
+    c->adab = cfg->n_layers > 0 ? find(c->man, "blocks.0.ada.bias") : find(c->man, "final.ada.bias");
+    c->outw = find(c->man, "final.out.weight");
+    c->outb = find(c->man, "final.out.bias");
+    char nm[64];
+    for (int l = 0; l < cfg->n_layers; ++l) {
+        cfm_ctx::LayerW L;
+        auto s = [&](const char* part, const char* kind) {
+            std::snprintf(nm, sizeof nm, "blocks.%d.%s.%s", l, part, kind);
+            return find(c->man, nm);
+        };
+        L.qkvw = s("qkv", "weight"); L.qkvb = s("qkv", "bias");
+        L.projw = s("proj", "weight"); L.projb = s("proj", "bias");
+        L.fc1w = s("fc1", "weight"); L.fc1b = s("fc1", "bias");
+        L.fc2w = s("fc2", "weight"); L.fc2b = s("fc2", "bias");
+        c->layers.push_back(L);
+    }
+    *out_ctx = c;
+    return CFM_OK;
+}
+
+void cfm_destroy(cfm_ctx* c) {
+    if (c == nullptr) return;
+    for (auto e : c->ev0) (void)hipEventDestroy(e);
+    for (auto e : c->ev1) (void)hipEventDestroy(e);
+    delete c;
+}
+
+cfm_status cfm_profile_enable(cfm_ctx* c, int kernel_class, int capacity) {
+    if (c == nullptr) return fail(CFM_E_NULL, "ctx is NULL");
+    if (kernel_class < 0 || kernel_class >= CFM_K_COUNT || capacity < 0)
+        return fail(CFM_E_VALUE, "bad kernel class or capacity");
+    while ((int)c->ev0.size() < capacity) {
+        hipEvent_t a, b;
+        if (hipEventCreate(&a) != hipSuccess) return fail(CFM_E_HIP, "hipEventCreate failed");
+        if (hipEventCreate(&b) != hipSuccess) { (void)hipEventDestroy(a); return fail(CFM_E_HIP, "hipEventCreate failed"); }
+        c->ev0.push_back(a);
+        c->ev1.push_back(b);
+    }
+    c->prof_class = kernel_class;
+    c->prof_cap = capacity;
+    c->prof_used = 0;
+    c->prof_dropped = 0;
+    return CFM_OK;
+}
+
+cfm_status cfm_profile_read(cfm_ctx* c, double* total_ms, int* launches, int* dropped) {
+    if (c == nullptr || total_ms == nullptr || launches == nullptr || dropped == nullptr)
+        return fail(CFM_E_NULL, "NULL argument");
+    double sum = 0.0;
+    for (int i = 0; i < c->prof_used; ++i) {
+        if (hipEventSynchronize(c->ev1[i]) != hipSuccess) return fail(CFM_E_HIP, "hipEventSynchronize failed");
+        float ms = 0.0f;
+        if (hipEventElapsedTime(&ms, c->ev0[i], c->ev1[i]) != hipSuccess)
+            return fail(CFM_E_HIP, "hipEventElapsedTime failed");
+        sum += ms;
+    }
+    *total_ms = sum;
+    *launches = c->prof_used;
+    *dropped = c->prof_dropped;
+    return CFM_OK;
+}
+
+cfm_status cfm_profile_disable(cfm_ctx* c) {
+    if (c == nullptr) return fail(CFM_E_NULL, "ctx is NULL");
+    c->prof_class = -1;
+    return CFM_OK;
+}
+
+cfm_status cfm_sample(cfm_ctx* c, const float* x0, const float* cond, const float* spk,
+                      const uint8_t* frame_mask, int R, int Tx, int S,
+                      const float* guidance, float* out, void* stream) {
+    if (c == nullptr) return fail(CFM_E_NULL, "ctx is NULL");
+    const cfm_config& g = c->cfg;
+    if (R < 0 || Tx < 0 || S < 0) return fail(CFM_E_VALUE, "negative n_requests, n_frames or n_steps");
+    if (R > g.max_requests || Tx > g.max_frames || S > g.max_steps)
+        return fail(CFM_E_CAPACITY, "R=%d Tx=%d S=%d above capacity %d/%d/%d", R, Tx, S,
+                    g.max_requests, g.max_frames, g.max_steps);
+    const int nb = g.n_branches;
+    if (nb > 1 && guidance == nullptr) return fail(CFM_E_NULL, "guidance is NULL");
+    float scales[2] = {0.0f, 0.0f};
+    for (int i = 0; i < nb - 1; ++i) {
+        scales[i] = guidance[i];
+        if (!std::isfinite(scales[i])) return fail(CFM_E_VALUE, "guidance scale %d is not finite", i);
+    }
+    if (R == 0 || Tx == 0) return CFM_OK;
+    if (x0 == nullptr || out == nullptr || cond == nullptr) return fail(CFM_E_NULL, "x0, cond or out is NULL");
+    if (g.spk_dim > 0 && spk == nullptr) return fail(CFM_E_NULL, "spk is NULL");
+    if (!aligned16(x0) || !aligned16(out) || !aligned16(cond) || (spk && !aligned16(spk)))
+        return fail(CFM_E_SHAPE, "x0, cond, spk and out must be 16-byte aligned");
+    const int C = g.latent_dim, d = g.d_model, L = g.n_layers;
+    const size_t xbytes = (size_t)R * Tx * C * sizeof(float);
+    {
+        const char* a = (const char*)x0;
+        const char* b = (const char*)out;
+        if (a != b && a < b + xbytes && b < a + xbytes)
+            return fail(CFM_E_SHAPE, "out partially overlaps x0 (only exact aliasing is allowed)");
+    }
+    hipStream_t s = (hipStream_t)stream;
+    (void)hipGetLastError();   // clear a stale error of an earlier, unrelated call
+    if (out != x0 && hipMemcpyAsync(out, x0, xbytes, hipMemcpyDeviceToDevice, s) != hipSuccess)
+        return fail(CFM_E_HIP, "hipMemcpyAsync failed");
+    if (S == 0) return CFM_OK;
+
+    const bool bf = g.dtype == CFM_BF16;
+    const bool prefix = g.cond_mode == CFM_COND_PREFIX;
+    const int P = prefix ? g.n_prefix : 0;
+    const int T = Tx + P, N = nb * R;
+    const long long NT = (long long)N * T;
+    const int cond0 = nb == 1 ? 0 : 1;
+    const int spk_branch = g.spk_dim > 0 ? nb - 1 : -1;
+    const int nc = 1 + (g.spk_dim > 0 ? R : 0);
+    const long long ML = (6LL * L + 2) * d;
+    const int H = g.n_heads, hd = d / H, f = g.ffn_dim;
+    const Layout& ly = c->lay;
+
+    float* h = wsp<float>(c, ly.h);
+    void* act = c->ws + ly.act;
+    void* big = c->ws + ly.big;
+    float* vel = wsp<float>(c, ly.v);
+    float* cproj = wsp<float>(c, ly.cproj);
+    float* temb = wsp<float>(c, ly.temb);
+    float* tpre = wsp<float>(c, ly.tpre);
+    float* ct = wsp<float>(c, ly.ct);
+    float* spkproj = wsp<float>(c, ly.spkproj);
+    float* cvec = wsp<float>(c, ly.cvec);
+    float* mod = wsp<float>(c, ly.mod);
+    int32_t* kvlen = wsp<int32_t>(c, ly.kvlen);
+
+    // GEMM through matrix cores (bf16 sampler) or fp32 FMA (fp32 sampler)
+    auto gemm = [&](int cls, bool a_f32, const void* A, int lda, Slot w, int M, int Nn, int K, int epi,
+                    const EpiParams& ep) {
+        timed(c, cls, s, [&] {
+            if (bf) launch_gemm_bf16(a_f32, epi, A, lda, wp<bf16>(c, w), w.ld, M, Nn, K, ep, s);
+            else launch_gemm_simt(false, false, epi, (const float*)A, lda, c->w + w.off, w.ld, M, Nn, K, ep, s);
+        });
+    };
+    // hoisted fp32-activation GEMMs against config-dtype weights
+    auto hoisted = [&](bool silu_a, const float* A, int lda, Slot w, Slot b, int M, int Nn, int K,
+                       float* o, long long ldo) {
+        EpiParams ep;
+        ep.bias = wp<float>(c, b);
+        ep.out = o;
+        ep.ldo = ldo;
+        timed(c, CFM_K_HOISTED, s, [&] {
+            launch_gemm_simt(bf, silu_a, EPI_F32, A, lda, c->w + w.off, w.ld, M, Nn, K, ep, s);
+        });
+    };
+
+    // ---- set-up, once per call
+    timed(c, CFM_K_HOISTED, s, [&] { launch_kv_len(frame_mask, R, Tx, P, kvlen, s); });
+    timed(c, CFM_K_HOISTED, s, [&] { launch_timestep_embedding(temb, S, g.t_freq_dim, s); });
+    hoisted(false, temb, g.t_freq_dim, c->t1w, c->t1b, S, d, g.t_freq_dim, tpre, d);
+    hoisted(true, tpre, d, c->t2w, c->t2b, S, d, d, ct, d);
+    if (g.spk_dim > 0) hoisted(false, spk, g.spk_dim, c->spkw, c->spkb, R, d, g.spk_dim, spkproj, d);
+    timed(c, CFM_K_HOISTED, s, [&] {
+        launch_assemble_cvec(ct, g.spk_dim > 0 ? wp<float>(c, c->spkb) : nullptr, spkproj, S, nc, d, cvec, s);
+    });
+    hoisted(true, cvec, d, c->adaw, c->adab, S * nc, (int)ML, d, mod, ML);
+    {
+        EpiParams ep;
+        ep.bias = wp<float>(c, c->inb);
+        ep.out = cproj;
+        ep.ldo = d;
+        if (prefix) gemm(CFM_K_HOISTED, true, cond, C, c->inxw, R * P, d, C, EPI_F32, ep);
+        else gemm(CFM_K_HOISTED, true, cond, g.cond_dim, c->incw, R * Tx, d, g.cond_dim, EPI_F32, ep);
+    }
+
+    auto rowmod = [&](const float* base, int tokens_per_row) {
+        RowMod m;
+        m.base = base;
+        m.cvec_stride = ML;
+        m.tokens_per_row = tokens_per_row;
+        m.n_requests = R;
+        m.spk_branch = spk_branch;
+        return m;
+    };
+    float w[3] = {1.0f, 0.0f, 0.0f};
+    if (nb == 2) { w[0] = 1.0f - scales[0]; w[1] = scales[0]; }
+    if (nb == 3) { w[0] = 1.0f - scales[0]; w[1] = scales[0] - scales[1]; w[2] = scales[1]; }
+
+    AttnParams ap;
+    ap.qkv = big; ap.o = act; ap.rows = N; ap.T = T; ap.H = H; ap.hd = hd;
+    ap.kv_len = kvlen; ap.kv_mod = R; ap.key_mask = frame_mask; ap.mask_stride = Tx; ap.P = P;
+
+    // ---- Euler steps
+    for (int k = 0; k < S; ++k) {
+        const double t0 = (double)k / S, t1 = (double)(k + 1) / S;
+        const float dt = (float)(t1 - t0);
+        const float* modk = mod + (long long)k * nc * ML;
+        if (prefix)
+            timed(c, CFM_K_GEMM_IN, s, [&] {
+                launch_prefix_init(cproj, wp<float>(c, c->inb), R, nb, cond0, P, T, d, h, s);
+            });
+        {
+            EpiParams ep;
+            ep.bias = wp<float>(c, c->inb);
+            ep.out = h; ep.ldo = d;
+            ep.R = R; ep.Tx = Tx; ep.T = T; ep.P = P; ep.nb = nb; ep.cond_branch0 = cond0;
+            ep.cproj = prefix ? nullptr : cproj;
+            gemm(CFM_K_GEMM_IN, true, out, C, c->inxw, R * Tx, d, C, EPI_INPROJ, ep);
+        }
+        for (int l = 0; l < L; ++l) {
+            const auto& W = c->layers[l];
+            const float* ml = modk + (long long)l * 6 * d;
+            LnParams ln;
+            ln.h = h; ln.y = act; ln.d = d; ln.n_out = NT; ln.Tin = T; ln.Tout = T; ln.off = 0;
+            ln.shift = rowmod(ml + 0 * d, T); ln.scale = rowmod(ml + 1 * d, T); ln.out_bf16 = bf;
+            timed(c, CFM_K_ADALN, s, [&] { launch_adaln(ln, s); });
+            EpiParams e1; e1.bias = wp<float>(c, W.qkvb); e1.out = big; e1.ldo = 3 * d;
+            gemm(CFM_K_GEMM_QKV, false, act, d, W.qkvw, (int)NT, 3 * d, d, EPI_ACT, e1);
+            timed(c, CFM_K_ATTENTION, s, [&] {
+                if (bf) launch_attention_bf16(ap, s); else launch_attention_f32(ap, s);
+            });
+            EpiParams e2; e2.bias = wp<float>(c, W.projb); e2.out = h; e2.ldo = d; e2.gate = rowmod(ml + 2 * d, T);
+            gemm(CFM_K_GEMM_PROJ, false, act, d, W.projw, (int)NT, d, d, EPI_GATED, e2);
+            ln.shift = rowmod(ml + 3 * d, T); ln.scale = rowmod(ml + 4 * d, T);
+            timed(c, CFM_K_ADALN, s, [&] { launch_adaln(ln, s); });
+            EpiParams e3; e3.bias = wp<float>(c, W.fc1b); e3.out = big; e3.ldo = f;
+            gemm(CFM_K_GEMM_FC1, false, act, d, W.fc1w, (int)NT, f, d, EPI_GELU_ACT, e3);
+            EpiParams e4; e4.bias = wp<float>(c, W.fc2b); e4.out = h; e4.ldo = d; e4.gate = rowmod(ml + 5 * d, T);
+            gemm(CFM_K_GEMM_FC2, false, big, f, W.fc2w, (int)NT, d, f, EPI_GATED, e4);
+        }
+        {
+            const float* mf = modk + (long long)L * 6 * d;
+            LnParams ln;
+            ln.h = h; ln.y = act; ln.d = d; ln.n_out = (long long)N * Tx; ln.Tin = T; ln.Tout = Tx; ln.off = P;
+            ln.shift = rowmod(mf, Tx); ln.scale = rowmod(mf + d, Tx); ln.out_bf16 = bf;
+            timed(c, CFM_K_ADALN, s, [&] { launch_adaln(ln, s); });
+            EpiParams ep; ep.bias = wp<float>(c, c->outb); ep.out = vel; ep.ldo = C;
+            ep.R = R; ep.Tx = Tx; ep.mask = frame_mask;
+            gemm(CFM_K_GEMM_OUT, false, act, d, c->outw, N * Tx, C, d, EPI_VOUT, ep);
+        }
+        timed(c, CFM_K_CFG_EULER, s, [&] {
+            launch_cfg_euler(vel, nb, dt * w[0], dt * w[1], dt * w[2], frame_mask, R, Tx, C, out, s);
+        });
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(CFM_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return CFM_OK;
+}
+
+// ------------------------------------------------------------ single kernels
+
+cfm_status cfm_cfg_euler(const float* v, const float* w, int nb, float dt, const uint8_t* mask,
+                         int R, int Tx, int C, float* x, void* stream) {
+    if (nb < 1 || nb > 3 || R < 0 || Tx < 0 || C < 0) return fail(CFM_E_VALUE, "bad nb/R/Tx/C");
+    if (C % 4) return fail(CFM_E_SHAPE, "C must be a multiple of 4");
+    if ((long long)R * Tx * C == 0) return CFM_OK;
+    if (v == nullptr || w == nullptr || x == nullptr) return fail(CFM_E_NULL, "v, w or x is NULL");
+    if (!aligned16(v) || !aligned16(x)) return fail(CFM_E_SHAPE, "v and x must be 16-byte aligned");
+    float ww[3] = {0.0f, 0.0f, 0.0f};
+    for (int b = 0; b < nb; ++b) {
+        if (!std::isfinite(w[b])) return fail(CFM_E_VALUE, "non-finite branch weight");
+        ww[b] = dt * w[b];
+    }
+    if (!std::isfinite(dt)) return fail(CFM_E_VALUE, "non-finite dt");
+    (void)hipGetLastError();
+    launch_cfg_euler(v, nb, ww[0], ww[1], ww[2], mask, R, Tx, C, x, (hipStream_t)stream);
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? CFM_OK : fail(CFM_E_HIP, "launch failed: %s", hipGetErrorString(e));
+}
+
+cfm_status cfm_gemm_bf16(const void* A, int a_is_f32, int lda, const void* W, int ldw,
+                         const float* bias, int M, int N, int K, int epilogue,
+                         const float* gate, void* C, int ldc, void* stream) {
+    if (M < 0 || N < 0 || K < 0) return fail(CFM_E_VALUE, "negative size");
+    if (epilogue < 0 || epilogue > 3) return fail(CFM_E_VALUE, "epilogue %d", epilogue);
+    if (M == 0 || N == 0) return CFM_OK;
+    if (A == nullptr || W == nullptr || C == nullptr) return fail(CFM_E_NULL, "A, W or C is NULL");
+    if (epilogue == 3 && gate == nullptr) return fail(CFM_E_NULL, "gate is NULL");
+    const int kq = a_is_f32 ? 4 : 8;
+    if (K % kq || lda % kq || ldw % 8 || lda < K || ldw < round8(K) || ldc < N)
+        return fail(CFM_E_SHAPE, "K/lda/ldw/ldc do not meet the layout rules");
+    if (!aligned16(A) || !aligned16(W)) return fail(CFM_E_SHAPE, "A and W must be 16-byte aligned");
+    static const int map[4] = {EPI_F32, EPI_ACT, EPI_GELU_ACT, EPI_GATED};
+    EpiParams ep;
+    ep.bias = bias;
+    ep.out = C;
+    ep.ldo = ldc;
+    ep.gate.base = gate;
+    ep.gate.cvec_stride = 0;
+    ep.gate.tokens_per_row = 1;
+    ep.gate.n_requests = 1;
+    ep.gate.spk_branch = -1;
+    (void)hipGetLastError();
+    launch_gemm_bf16(a_is_f32 != 0, map[epilogue], A, lda, (const bf16*)W, ldw, M, N, K, ep, (hipStream_t)stream);
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? CFM_OK : fail(CFM_E_HIP, "launch failed: %s", hipGetErrorString(e));
+}
+
+cfm_status cfm_attention_bf16(const void* qkv, const int32_t* kv_len, const uint8_t* key_mask,
+                              int rows, int T, int H, void* o, void* stream) {
+    if (rows < 0 || T < 0 || H <= 0) return fail(CFM_E_VALUE, "bad rows/T/H");
+    if (rows > 65535 || H > 65535) return fail(CFM_E_SHAPE, "rows and H must be <= 65535");
+    if (rows == 0 || T == 0) return CFM_OK;
+    if (qkv == nullptr || kv_len == nullptr || o == nullptr) return fail(CFM_E_NULL, "qkv, kv_len or o is NULL");
+    if (!aligned16(qkv) || ((uintptr_t)o & 7)) return fail(CFM_E_SHAPE, "qkv 16-byte / o 8-byte alignment");
+    AttnParams p;
+    p.qkv = qkv; p.o = o; p.rows = rows; p.T = T; p.H = H; p.hd = 64;
+    p.kv_len = kv_len; p.kv_mod = rows; p.key_mask = key_mask; p.mask_stride = T; p.P = 0;
+    (void)hipGetLastError();
+    launch_attention_bf16(p, (hipStream_t)stream);
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? CFM_OK : fail(CFM_E_HIP, "launch failed: %s", hipGetErrorString(e));
+}
+
+cfm_status cfm_adaln(const float* hsrc, const float* shift, const float* scale, int M, int d,
+                     int out_bf16, void* y, void* stream) {
+    if (M < 0 || d <= 0) return fail(CFM_E_VALUE, "bad M/d");
+    if (d % 4 || d > 4096) return fail(CFM_E_SHAPE, "d must be a multiple of 4 and <= 4096");
+    if (M == 0) return CFM_OK;
+    if (hsrc == nullptr || shift == nullptr || scale == nullptr || y == nullptr) return fail(CFM_E_NULL, "NULL argument");
+    if (!aligned16(hsrc) || !aligned16(shift) || !aligned16(scale) || ((uintptr_t)y & 7))
+        return fail(CFM_E_SHAPE, "alignment");
+    LnParams p;
+    p.h = hsrc; p.y = y; p.d = d; p.n_out = M; p.Tin = 1; p.Tout = 1; p.off = 0;
+    p.shift.base = shift; p.shift.cvec_stride = 0; p.shift.tokens_per_row = 1; p.shift.n_requests = 1; p.shift.spk_branch = -1;
+    p.scale = p.shift;
+    p.scale.base = scale;
+    p.out_bf16 = out_bf16 != 0;
+    (void)hipGetLastError();
+    launch_adaln(p, (hipStream_t)stream);
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? CFM_OK : fail(CFM_E_HIP, "launch failed: %s", hipGetErrorString(e));
+}
+
+}  // extern "C"

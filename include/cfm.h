@@ -1,0 +1,204 @@
+/*
+ * cfm.h -- C ABI of the MI355X (gfx950) batched conditional-flow-matching sampler.
+ *
+ * What the library computes (sources: the VoiceHub page "Diffusion and flow TTS
+ * optimization", sections "Active families", "Custom Triton and CUDA kernels",
+ * "Static shapes and CUDA graphs" and its table "Semantic-preserving and
+ * approximate changes"; the vLLM-Omni TTS blog, section "CFM/LocDiT decode-tail
+ * batching"):
+ *
+ *   Euler sampling of a flow-matching / rectified-flow ODE from noise x0 (t = 0)
+ *   to data (t = 1) on the uniform grid t_k = k / S. At every step one DiT
+ *   velocity estimator runs over ALL requests of the batch at once, each request
+ *   expanded into its classifier-free-guidance branch rows ("packed CFG": rows
+ *   are branch-major, row = b * R + r). The branch velocities are combined with
+ *   the guidance equation and the Euler update x <- x + dt * v is applied:
+ *
+ *     2 branches (uncond, cond):            v = v_u + s (v_c - v_u)
+ *     3 branches (uncond, text, text+spk):  v = v_u + s_t (v_t - v_u) + s_s (v_ts - v_t)
+ *     1 branch:                             v = v_c
+ *
+ *   Estimator per row: c = W2 SiLU(W1 e(t) + b1) + b2 (+ Ws spk + bs), e(t) the
+ *   256-wide sinusoidal embedding of 1000 t; h = input projection of the frames
+ *   (latent channels concatenated with per-frame condition channels, or
+ *   condition frames placed before the latent frames); L DiT blocks, each
+ *     h += gate1 * Proj(MHA(LN(h) (1 + scale1) + shift1))
+ *     h += gate2 * FC2(GELU(FC1(LN(h) (1 + scale2) + shift2)))
+ *   with (shift1, scale1, gate1, shift2, scale2, gate2) = Wada_l SiLU(c) + bada_l,
+ *   key-padding-masked non-causal attention; v = Out(LN(h)(1 + scale_f) + shift_f).
+ *   Branches without a condition see it zeroed. Padded frames are masked as keys,
+ *   get v = 0, and are returned unchanged (out = x0 there, bit for bit).
+ *
+ * Conventions for every function:
+ *   - All device pointers are HIP device (or managed) memory on the current
+ *     device; host pointers are marked "host". Tensors are dense row-major.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). Work
+ *     is enqueued asynchronously on it; no function here synchronises the host,
+ *     allocates device memory or reads device memory back, except where stated.
+ *   - Every argument is validated BEFORE anything is enqueued: on an error
+ *     return nothing was launched and no output was touched. Errors detected
+ *     after enqueue (a failed launch) return CFM_E_HIP and leave outputs
+ *     undefined. No function aborts or throws. The detail of the last error of
+ *     the calling thread is available from cfm_last_error_detail().
+ *   - A context is not safe for concurrent cfm_sample calls (they share its
+ *     workspace); separate contexts are independent.
+ */
+#ifndef CFM_MI355X_H
+#define CFM_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum cfm_status {
+    CFM_OK = 0,
+    CFM_E_NULL = 1,          /* a required pointer is NULL                          */
+    CFM_E_SHAPE = 2,         /* inconsistent sizes or layout                        */
+    CFM_E_CAPACITY = 3,      /* request/frame/step count above the create-time max  */
+    CFM_E_VALUE = 4,         /* negative count, non-finite guidance scale, ...      */
+    CFM_E_UNSUPPORTED = 5,   /* configuration this build does not implement         */
+    CFM_E_WORKSPACE = 6,     /* workspace smaller than cfm_workspace_bytes()        */
+    CFM_E_HIP = 7            /* a HIP runtime call or kernel launch failed          */
+} cfm_status;
+
+typedef enum cfm_dtype { CFM_F32 = 0, CFM_BF16 = 1 } cfm_dtype;
+typedef enum cfm_cond_mode { CFM_COND_CHANNEL = 0, CFM_COND_PREFIX = 1 } cfm_cond_mode;
+
+/* Model and capacity description. Plain data; copied by cfm_create.
+ *   cond_mode CHANNEL: cond is [R, Tx, cond_dim], concatenated after the latent
+ *                      channels of each frame before the input projection.
+ *   cond_mode PREFIX:  cond is [R, n_prefix, latent_dim]: condition frames placed
+ *                      before the Tx latent frames (cond_dim must equal latent_dim).
+ *   dtype BF16: weights and GEMM/attention operands bfloat16 with fp32
+ *               accumulation; residual stream, LayerNorm statistics, softmax,
+ *               modulation, velocities and x are fp32.
+ *   dtype F32:  fp32 end to end.
+ * Supported: d_model % 8 == 0, ffn_dim % 8 == 0, latent_dim % 4 == 0,
+ * cond_dim % 4 == 0, t_freq_dim even and % 8 == 0, 1 <= n_branches <= 3;
+ * BF16 needs head_dim == 64, F32 needs head_dim % 4 == 0 and head_dim <= 128. */
+typedef struct cfm_config {
+    int32_t n_layers, d_model, n_heads, ffn_dim;
+    int32_t latent_dim, cond_dim, cond_mode, n_prefix;
+    int32_t spk_dim;          /* 0 = no speaker path                                 */
+    int32_t t_freq_dim;       /* width of the sinusoidal timestep embedding (256)   */
+    int32_t n_branches;       /* CFG branch rows per request: 1, 2 or 3             */
+    int32_t dtype;            /* cfm_dtype                                          */
+    int32_t max_requests, max_frames, max_steps;   /* capacity of the workspace    */
+} cfm_config;
+
+/* One slot of the flat weight buffer. The slot holds
+ * source[row0 : row0 + rows, col0 : col0 + cols] of the named parameter
+ * (PyTorch Linear convention: weight [out, in], bias [out]) with a row stride
+ * of `ld` elements, starting `offset` bytes into the buffer. `dtype` is the
+ * element type of the slot (matrices: the config dtype; biases: always F32).
+ * Bytes of the buffer not covered by a slot (row padding) must be zero. */
+typedef struct cfm_tensor_desc {
+    char name[48];
+    int64_t row0, col0, rows, cols, ld;
+    int64_t offset;
+    int32_t dtype;
+    int32_t reserved;
+} cfm_tensor_desc;
+
+typedef struct cfm_ctx cfm_ctx;
+
+/* Host-only size queries. Return 0 / a negative cfm_status for an unsupported
+ * or invalid config. */
+size_t cfm_weights_bytes(const cfm_config* cfg);
+size_t cfm_workspace_bytes(const cfm_config* cfg);
+/* Writes up to `cap` slot descriptors to `out` (host) and returns the total
+ * number of slots, or -(cfm_status) on error. out may be NULL when cap == 0. */
+int cfm_weight_manifest(const cfm_config* cfg, cfm_tensor_desc* out, int cap);
+
+/* Creates a sampler context (host memory only; no HIP call). BORROWS
+ * `weights` (cfm_weights_bytes, filled per the manifest) and `workspace`
+ * (cfm_workspace_bytes): both are caller-owned device memory that must outlive
+ * the context and every call still in flight. Errors: CFM_E_NULL,
+ * CFM_E_UNSUPPORTED, CFM_E_VALUE, CFM_E_WORKSPACE. */
+cfm_status cfm_create(const cfm_config* cfg, const void* weights, void* workspace,
+                      size_t workspace_bytes, cfm_ctx** out_ctx);
+
+/* Runs the whole sampler: S = n_steps Euler steps over R = n_requests requests.
+ *   x0         device fp32 [R, Tx, latent_dim]         noise (t = 0)
+ *   cond       device fp32 [R, Tx, cond_dim] (CHANNEL) or [R, n_prefix, latent_dim] (PREFIX)
+ *   spk        device fp32 [R, spk_dim], or NULL when spk_dim == 0
+ *   frame_mask device uint8 [R, Tx], 1 = valid frame, or NULL = all valid
+ *   guidance   host fp32 [n_branches - 1] guidance scales (NULL allowed when n_branches == 1)
+ *   out        device fp32 [R, Tx, latent_dim]; may alias x0 exactly
+ * Tx = n_frames. R == 0 is a no-op; S == 0 gives out = x0. A request with no
+ * valid frame gives out = x0. Inputs must stay alive and unmodified until the
+ * stream has passed this call. Errors: CFM_E_NULL, CFM_E_SHAPE, CFM_E_CAPACITY,
+ * CFM_E_VALUE (negative count, non-finite scale), CFM_E_HIP. */
+cfm_status cfm_sample(cfm_ctx* ctx, const float* x0, const float* cond, const float* spk,
+                      const uint8_t* frame_mask, int n_requests, int n_frames, int n_steps,
+                      const float* guidance, float* out, void* stream);
+
+/* Frees host state only (the borrowed buffers stay the caller's). NULL-safe. */
+void cfm_destroy(cfm_ctx* ctx);
+
+const char* cfm_status_string(cfm_status s);
+/* Thread-local text describing the last error returned on this thread. */
+const char* cfm_last_error_detail(void);
+
+/* ---------------------------------------------------------------------------
+ * Kernel timing. While enabled, every launch of the selected kernel class is
+ * bracketed by two hipEvents recorded on the launch stream. cfm_profile_read
+ * SYNCHRONISES on those events (host wait) and returns the summed elapsed
+ * milliseconds and the launch count since the last enable; the event pool holds
+ * `capacity` launches (extra launches are not timed and counted in *dropped).
+ * Class ids are the CFM_K_* values below. */
+enum {
+    CFM_K_GEMM_QKV = 0, CFM_K_GEMM_PROJ = 1, CFM_K_GEMM_FC1 = 2, CFM_K_GEMM_FC2 = 3,
+    CFM_K_ATTENTION = 4, CFM_K_ADALN = 5, CFM_K_CFG_EULER = 6, CFM_K_GEMM_IN = 7,
+    CFM_K_GEMM_OUT = 8, CFM_K_HOISTED = 9, CFM_K_COUNT = 10
+};
+cfm_status cfm_profile_enable(cfm_ctx* ctx, int kernel_class, int capacity);
+cfm_status cfm_profile_read(cfm_ctx* ctx, double* total_ms, int* launches, int* dropped);
+cfm_status cfm_profile_disable(cfm_ctx* ctx);
+
+/* ---------------------------------------------------------------------------
+ * Single-kernel entry points (the same kernels cfm_sample launches), for
+ * kernel-level parity tests and roofline measurement.
+ *
+ * Fused CFG combine + Euler update (VoiceHub, "Custom Triton and CUDA kernels":
+ * packed CFG combination plus an Euler update):
+ *   for every valid frame (r, t): x[r,t,:] += dt * sum_b w[b] * v[b,r,t,:]
+ * v device fp32 [nb, R, Tx, C]; w host fp32 [nb] branch weights (for guidance
+ * scale s: w = (1 - s, s); three branches: (1 - s_t, s_t - s_s, s_s));
+ * mask device uint8 [R, Tx] or NULL; x device fp32 [R, Tx, C] updated in place.
+ * Masked frames of x are not written. C % 4 == 0. */
+cfm_status cfm_cfg_euler(const float* v, const float* w, int nb, float dt, const uint8_t* mask,
+                         int R, int Tx, int C, float* x, void* stream);
+
+/* bf16 MFMA GEMM with a plain epilogue: C[m,n] = sum_k A[m,k] W[n,k] + bias[n].
+ *   A device bf16 (a_is_f32 = 0) or fp32 (a_is_f32 = 1, rounded to bf16 on load)
+ *   [M, K] row stride lda; W device bf16 [N, K] row stride ldw; bias device fp32
+ *   [N] or NULL. epilogue 0: C fp32; 1: C bf16; 2: C bf16 of GELU(exact erf);
+ *   3: gated residual C(fp32) += gate[n] * (acc + bias[n]) with gate device fp32 [N].
+ * K % 8 == 0 (bf16 A) or K % 4 == 0 (fp32 A); lda, ldw multiples of 8 (bf16)
+ * or 4 (fp32 A); ldw >= K rounded up to 8 with zero padding. */
+cfm_status cfm_gemm_bf16(const void* A, int a_is_f32, int lda, const void* W, int ldw,
+                         const float* bias, int M, int N, int K, int epilogue,
+                         const float* gate, void* C, int ldc, void* stream);
+
+/* Key-padding-masked multi-head attention, bf16 in / bf16 out, fp32 softmax.
+ *   qkv device bf16 [rows, T, 3 * H * 64] (q | k | v, head j at columns j*64)
+ *   kv_len device int32 [rows]: keys >= kv_len[row] are masked;
+ *   key_mask device uint8 [rows, T] (1 = valid key) or NULL;
+ *   o device bf16 [rows, T, H * 64]. A row with no valid key gives o = 0. */
+cfm_status cfm_attention_bf16(const void* qkv, const int32_t* kv_len, const uint8_t* key_mask,
+                              int rows, int T, int H, void* o, void* stream);
+
+/* adaLN-modulated LayerNorm: y = LN(h) * (1 + scale) + shift, eps 1e-6, biased
+ * variance, stats in fp32. h device fp32 [M, d]; shift, scale device fp32 [d];
+ * y device bf16 (out_bf16 = 1) or fp32 [M, d]. d % 4 == 0. */
+cfm_status cfm_adaln(const float* h, const float* shift, const float* scale, int M, int d,
+                     int out_bf16, void* y, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CFM_MI355X_H */

@@ -1,0 +1,155 @@
+"""The C ABI on the host (no GPU): exports, size queries, manifest, and argument
+validation that must fail before anything is enqueued."""
+import ctypes as C
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+import synth
+from tests.helpers import config_for
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import flow_matching_tts_amd as F
+    try:
+        return F.load()
+    except ImportError as e:
+        pytest.fail(f"library not built: {e}")
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "cfm.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(cfm_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_function_is_exported(lib):
+    import flow_matching_tts_amd as F
+    names = header_functions()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(F.EXPORTS) == names
+
+
+def test_status_strings(lib):
+    for s in range(8):
+        assert lib.cfm_status_string(s)
+    assert lib.cfm_status_string(99) == b"unknown status"
+
+
+@pytest.mark.parametrize("name", synth.WORKLOAD_ORDER)
+def test_sizes_and_manifest_cover_every_parameter(lib, name):
+    import flow_matching_tts_amd as F
+    s = synth.workload(name)
+    cfg = config_for(s)
+    wb, ws = F.weights_bytes(cfg), F.workspace_bytes(cfg)
+    assert wb > 0 and ws > 0 and wb % 256 == 0
+    man = F.weight_manifest(cfg)
+    specs = dict(synth.weight_specs(s))
+    covered = {}
+    es = {0: 4, 1: 2}
+    spans = []
+    for e in man:
+        shp = specs[e["name"]]
+        rows, cols = (1, shp[0]) if len(shp) == 1 else shp
+        assert e["row0"] + e["rows"] <= rows and e["col0"] + e["cols"] <= cols
+        assert e["ld"] >= e["cols"] and e["offset"] % (2 if e["dtype"] == 1 else 4) == 0
+        if e["dtype"] == 1 and len(shp) == 2:
+            assert e["ld"] % 8 == 0
+        covered[e["name"]] = covered.get(e["name"], 0) + e["rows"] * e["cols"]
+        spans.append((e["offset"], e["offset"] + e["rows"] * e["ld"] * es[e["dtype"]]))
+    for n, shp in specs.items():
+        assert covered.get(n) == int(np.prod(shp)), n
+    spans.sort()
+    for (a0, a1), (b0, b1) in zip(spans, spans[1:]):
+        assert a1 <= b0
+    assert spans[-1][1] <= wb
+
+
+def test_pack_weights_places_every_value(lib):
+    import flow_matching_tts_amd as F
+    s = synth.workload("tiny_f32")
+    cfg = config_for(s)
+    W = synth.make_weights(s)
+    buf = F.pack_weights(cfg, W)
+    for e in F.weight_manifest(cfg):
+        src = W[e["name"]].reshape(-1, W[e["name"]].shape[-1]) if W[e["name"]].ndim == 2 else W[e["name"]][None]
+        blk = buf[e["offset"]:e["offset"] + e["rows"] * e["ld"] * 4].view(np.float32).reshape(e["rows"], e["ld"])
+        np.testing.assert_array_equal(blk[:, :e["cols"]], src[e["row0"]:e["row0"] + e["rows"], e["col0"]:e["col0"] + e["cols"]])
+
+
+def _cfg(**kw):
+    s = synth.workload("mel_dit").replace(**kw) if kw else synth.workload("mel_dit")
+    return config_for(s)
+
+
+def test_create_validation(lib):
+    ctx = C.c_void_p()
+    cfg = _cfg()
+    fake = 1 << 20   # never dereferenced: cfm_create only records pointers
+    ws = lib.cfm_workspace_bytes(C.byref(cfg))
+    assert lib.cfm_create(C.byref(cfg), None, fake, ws, C.byref(ctx)) == 1
+    assert lib.cfm_create(C.byref(cfg), fake, fake, ws - 1, C.byref(ctx)) == 6
+    assert lib.cfm_create(C.byref(cfg), fake + 16, fake, ws, C.byref(ctx)) == 2
+    assert lib.cfm_create(None, fake, fake, ws, C.byref(ctx)) == 1
+    bad = _cfg(n_heads=8)            # head_dim 128 on the bf16 path
+    assert lib.cfm_create(C.byref(bad), fake, fake, ws, C.byref(ctx)) == 5
+    assert b"head_dim" in lib.cfm_last_error_detail()
+    bad = _cfg(n_branches=4)
+    assert lib.cfm_create(C.byref(bad), fake, fake, ws, C.byref(ctx)) == 5
+    bad = _cfg(latent_dim=98)
+    assert lib.cfm_weights_bytes(C.byref(bad)) == 0
+    assert lib.cfm_create(C.byref(cfg), fake, fake, ws, C.byref(ctx)) == 0 and ctx.value
+    lib.cfm_destroy(ctx)
+    lib.cfm_destroy(None)
+
+
+def test_sample_validation_fails_before_any_device_work(lib):
+    cfg = _cfg()
+    fake = 1 << 20
+    ws = lib.cfm_workspace_bytes(C.byref(cfg))
+    ctx = C.c_void_p()
+    assert lib.cfm_create(C.byref(cfg), fake, fake, ws, C.byref(ctx)) == 0
+    g = (C.c_float * 1)(2.0)
+    x, cond, out = 1 << 24, 1 << 26, 1 << 28
+    R, T, S = 8, 1000, 32
+    call = lambda **k: lib.cfm_sample(ctx, k.get("x0", x), k.get("cond", cond), None, None,
+                                      k.get("R", R), k.get("T", T), k.get("S", S), k.get("g", g),
+                                      k.get("out", out), None)
+    assert call(R=-1) == 4
+    assert call(S=-2) == 4
+    assert call(R=9) == 3
+    assert call(T=1001) == 3
+    assert call(S=33) == 3
+    assert call(g=None) == 1
+    assert call(g=(C.c_float * 1)(math.inf)) == 4
+    assert call(g=(C.c_float * 1)(math.nan)) == 4
+    assert call(x0=None) == 1
+    assert call(cond=None) == 1
+    assert call(out=None) == 1
+    assert call(x0=x + 4) == 2                          # misaligned
+    assert call(out=x + 16) == 2                        # partial overlap with x0
+    assert call(R=0) == 0 and call(R=0, x0=None) == 0   # empty batch: no-op
+    assert call(T=0) == 0
+    lib.cfm_destroy(ctx)
+
+
+def test_single_kernel_entry_validation(lib):
+    g = (C.c_float * 2)(0.5, 0.5)
+    assert lib.cfm_cfg_euler(None, g, 2, C.c_float(0.1), None, 2, 3, 4, None, None) == 1
+    assert lib.cfm_cfg_euler(1 << 20, g, 2, C.c_float(0.1), None, 2, 3, 6, 1 << 21, None) == 2
+    assert lib.cfm_cfg_euler(1 << 20, g, 4, C.c_float(0.1), None, 2, 3, 4, 1 << 21, None) == 4
+    assert lib.cfm_cfg_euler(None, g, 2, C.c_float(0.1), None, 0, 3, 4, None, None) == 0
+    assert lib.cfm_gemm_bf16(1 << 20, 0, 12, 1 << 21, 16, None, 4, 4, 12, 0, None, 1 << 22, 4, None) == 2
+    assert lib.cfm_gemm_bf16(1 << 20, 0, 16, 1 << 21, 16, None, 4, 4, 16, 3, None, 1 << 22, 4, None) == 1
+    assert lib.cfm_gemm_bf16(1 << 20, 0, 16, 1 << 21, 16, None, 4, 4, 16, 9, None, 1 << 22, 4, None) == 4
+    assert lib.cfm_attention_bf16(None, None, None, 2, 8, 1, None, None) == 1
+    assert lib.cfm_attention_bf16(None, None, None, 0, 8, 1, None, None) == 0
+    assert lib.cfm_adaln(1 << 20, 1 << 21, 1 << 22, 4, 30, 0, 1 << 23, None) == 2

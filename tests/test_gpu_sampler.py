@@ -1,0 +1,181 @@
+"""End-to-end parity of cfm_sample against the CPU oracle, and its invariants (GPU only).
+
+Tolerance (relative L2 over all valid frames, after all steps): 1e-4 on the
+fp32 path, 2e-2 on the bf16 path.
+
+* reduced workloads: the shape family of each of the five benchmark cases at a
+  size the oracle finishes in seconds, still spanning several GEMM and
+  attention tiles with ragged tails; the oracle runs inside the test;
+* full-size workloads, in the launch configuration of the benchmark: sampled
+  requests are compared with oracle outputs stored by
+  tests/golden/make_oracle_refs.py (written by the oracle alone);
+* invariants from the pages' batching rules (VoiceHub "Diffusion and flow TTS
+  optimization", table "Semantic-preserving and approximate changes"): packed
+  CFG equals separate branch calls, guidance scale 1 / 0 equal the conditional /
+  unconditional branch alone, padded frames are returned untouched, request
+  permutation permutes the outputs, repeat runs are bitwise identical.
+"""
+import hashlib
+import os
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import sampler as O
+from tests.helpers import TOL, config_for, dev, rel_l2, run_sampler
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import flow_matching_tts_amd as F
+    F.load()
+
+
+def reduced(name):
+    s = synth.workload(name)
+    if name == "tiny_f32":
+        return s
+    if name == "locdit_tail":
+        return s.replace(n_requests=9, n_steps=3, n_layers=2)
+    if name == "mel_dit":
+        return s.replace(n_layers=2, n_frames=300, n_requests=2, n_steps=3)
+    if name == "varlen_masked":
+        return s.replace(n_layers=2, n_frames=400, n_requests=3, n_steps=3, varlen=(50, 400))
+    if name == "multicond_rf":
+        return s.replace(n_layers=2, n_frames=200, n_requests=2, n_steps=3)
+    raise KeyError(name)
+
+
+def _valid(I, s):
+    if I["mask"] is None:
+        return np.ones((s.n_requests, s.n_frames), bool)
+    return I["mask"].astype(bool)
+
+
+@pytest.mark.parametrize("name", synth.WORKLOAD_ORDER)
+def test_reduced_workload_matches_oracle(name):
+    s = reduced(name)
+    W, I = synth.make_weights(s, 100 + s.index), synth.make_inputs(s, 200 + s.index)
+    got, _ = run_sampler(s, W, I)
+    want = O.sample(W, s, I["x0"], I["cond"], I["spk"], I["mask"], s.n_steps, s.guidance)
+    valid = _valid(I, s)
+    err = rel_l2(got, want, valid)
+    disp = rel_l2(got - I["x0"], want - I["x0"], valid)
+    print(f"{name}: rel-L2 {err:.3e} (displacement {disp:.3e})")
+    assert err <= TOL[s.dtype], (err, disp)
+    np.testing.assert_array_equal(got[~valid], I["x0"][~valid])
+
+
+def _golden(name):
+    path = os.path.join(GOLDEN, f"oracle_{name}.npz")
+    if not os.path.exists(path):
+        pytest.skip(f"{path} not generated")
+    z = np.load(path)
+    with open(os.path.join(os.path.dirname(GOLDEN), "..", "oracle", "sampler.py"), "rb") as f:
+        assert str(z["oracle_sha256"]) == hashlib.sha256(f.read()).hexdigest(), "stale oracle reference"
+    return z
+
+
+@pytest.mark.parametrize("name", synth.WORKLOAD_ORDER)
+def test_full_workload_matches_stored_oracle(name):
+    s = synth.workload(name)
+    z = _golden(name)
+    W, I = synth.make_weights(s), synth.make_inputs(s)
+    got, _ = run_sampler(s, W, I)
+    reqs, frames = z["requests"], z["frames"]
+    g = got[reqs][:, frames, :]
+    valid = _valid(I, s)[reqs][:, frames]
+    x0 = I["x0"][reqs][:, frames, :]
+    err = rel_l2(g, z["out"], valid)
+    disp = rel_l2(g - x0, z["out"] - x0, valid)
+    print(f"{name}: full size, requests {list(reqs)}: rel-L2 {err:.3e} (displacement {disp:.3e})")
+    assert err <= TOL[s.dtype], (err, disp)
+    # every request: finite, padded frames untouched
+    assert np.all(np.isfinite(got))
+    np.testing.assert_array_equal(got[~_valid(I, s)], I["x0"][~_valid(I, s)])
+
+
+def test_guidance_one_equals_conditional_branch_and_zero_the_unconditional():
+    s = reduced("mel_dit")
+    W, I = synth.make_weights(s, 301), synth.make_inputs(s, 302)
+    s1 = s.replace(n_branches=1, guidance=())
+    full1, _ = run_sampler(s, W, I, guidance=(1.0,))
+    cond_only, _ = run_sampler(s1, W, I)
+    np.testing.assert_allclose(full1, cond_only, rtol=0, atol=1e-6)
+    full0, _ = run_sampler(s, W, I, guidance=(0.0,))
+    I0 = dict(I, cond=np.zeros_like(I["cond"]))
+    uncond_only, _ = run_sampler(s1, W, I0)
+    np.testing.assert_allclose(full0, uncond_only, rtol=0, atol=1e-6)
+
+
+def test_three_branch_reductions_on_gpu():
+    s = reduced("multicond_rf")
+    W, I = synth.make_weights(s, 311), synth.make_inputs(s, 312)
+    ts_only, _ = run_sampler(s.replace(n_branches=1, guidance=()), W, I)
+    both_one, _ = run_sampler(s, W, I, guidance=(1.0, 1.0))
+    np.testing.assert_allclose(both_one, ts_only, rtol=0, atol=1e-6)
+
+
+def test_request_permutation_and_determinism():
+    s = reduced("varlen_masked")
+    W, I = synth.make_weights(s, 321), synth.make_inputs(s, 322)
+    a, smp = run_sampler(s, W, I)
+    b, _ = run_sampler(s, W, I, sampler=smp)
+    np.testing.assert_array_equal(a, b)
+    perm = np.array([2, 0, 1])
+    Ip = {k: (None if v is None else v[perm]) for k, v in I.items()}
+    c, _ = run_sampler(s, W, Ip, sampler=smp)
+    np.testing.assert_array_equal(c, a[perm])
+
+
+def test_padded_request_equals_unpadded_request():
+    s = reduced("varlen_masked").replace(n_requests=1)
+    W, I = synth.make_weights(s, 331), synth.make_inputs(s, 332)
+    n = 173
+    mask = np.zeros((1, s.n_frames), np.uint8)
+    mask[0, :n] = 1
+    padded, _ = run_sampler(s, W, I, mask=mask)
+    s_short = s.replace(n_frames=n, varlen=None)
+    I_short = dict(I, x0=I["x0"][:, :n].copy(), cond=I["cond"][:, :n].copy(), mask=None)
+    short, _ = run_sampler(s_short, W, I_short)
+    np.testing.assert_allclose(padded[:, :n], short, rtol=0, atol=2e-5)
+    np.testing.assert_array_equal(padded[:, n:], I["x0"][:, n:])
+
+
+def test_out_may_alias_x0_and_poisoned_workspace_changes_nothing():
+    s = reduced("multicond_rf")
+    W, I = synth.make_weights(s, 341), synth.make_inputs(s, 342)
+    a, smp = run_sampler(s, W, I)
+    smp.workspace.view(torch.float32).fill_(float("nan"))
+    b, _ = run_sampler(s, W, I, sampler=smp, out_alias=True)
+    np.testing.assert_array_equal(a, b)
+
+
+def test_zero_steps_and_zero_valid_frames():
+    s = reduced("mel_dit")
+    W, I = synth.make_weights(s, 351), synth.make_inputs(s, 352)
+    out0, smp = run_sampler(s, W, I, n_steps=0)
+    np.testing.assert_array_equal(out0, I["x0"])
+    mask = np.ones((s.n_requests, s.n_frames), np.uint8)
+    mask[1] = 0
+    out, _ = run_sampler(s, W, I, mask=mask, sampler=smp)
+    np.testing.assert_array_equal(out[1], I["x0"][1])
+    assert np.all(np.isfinite(out)) and np.abs(out[0] - I["x0"][0]).max() > 1e-3
+
+
+def test_fewer_requests_and_frames_than_capacity():
+    import flow_matching_tts_amd as F
+    s = reduced("mel_dit")
+    W = synth.make_weights(s, 361)
+    big = F.Sampler(config_for(s, max_requests=4, max_frames=400, max_steps=8), W)
+    I = synth.make_inputs(s, 362)
+    a, _ = run_sampler(s, W, I, sampler=big)
+    b, _ = run_sampler(s, W, I)
+    np.testing.assert_array_equal(a, b)
