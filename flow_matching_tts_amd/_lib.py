@@ -85,7 +85,7 @@ def load() -> C.CDLL:
     lib.cfm_profile_disable.restype = i32
     lib.cfm_cfg_euler.argtypes = [vp, f32p, i32, C.c_float, vp, i32, i32, i32, vp, vp]
     lib.cfm_cfg_euler.restype = i32
-    lib.cfm_gemm_bf16.argtypes = [vp, i32, i32, vp, i32, vp, i32, i32, i32, i32, vp, vp, i32, vp]
+    lib.cfm_gemm_bf16.argtypes = [vp, i32, i32, vp, i32, vp, i32, i32, i32, i32, vp, vp, i32, i32, vp]
     lib.cfm_gemm_bf16.restype = i32
     lib.cfm_attention_bf16.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp]
     lib.cfm_attention_bf16.restype = i32
@@ -229,7 +229,8 @@ def cfg_euler(v, w: Sequence[float], dt: float, x, mask=None, stream=None):
     return x
 
 
-def gemm_bf16(A, W, bias=None, *, epilogue: int, out, gate=None, K: Optional[int] = None, stream=None):
+def gemm_bf16(A, W, bias=None, *, epilogue: int, out, gate=None, K: Optional[int] = None, tile: int = 0,
+              stream=None):
     """out = epilogue(A[:, :K] W[:, :K]^T + bias); A bf16 or fp32, W bf16 [N, ldw]."""
     import torch
     M, lda = int(A.shape[0]), int(A.shape[1])
@@ -237,7 +238,7 @@ def gemm_bf16(A, W, bias=None, *, epilogue: int, out, gate=None, K: Optional[int
     K = lda if K is None else int(K)
     a_f32 = 1 if A.dtype == torch.float32 else 0
     check(load().cfm_gemm_bf16(_ptr(A), a_f32, lda, _ptr(W), ldw, _ptr(bias), M, N, K, int(epilogue),
-                               _ptr(gate), _ptr(out), int(out.shape[1]), _stream(stream)))
+                               _ptr(gate), _ptr(out), int(out.shape[1]), int(tile), _stream(stream)))
     return out
 
 

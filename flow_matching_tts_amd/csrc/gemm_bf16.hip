@@ -1,146 +1,191 @@
 // bf16 MFMA GEMM for gfx950: C[m, n] = sum_k A[m, k] W[n, k] with fused epilogues.
 //
 // Both operands are K-contiguous (A row-major [M, K], W in Linear layout
-// [N, K]), which is the natural operand order of v_mfma_f32_32x32x16_bf16:
-// every lane feeds 8 consecutive k of one A row and 8 consecutive k of one W
-// row, so LDS tiles are read with 16-byte loads and never transposed.
+// [N, K]), the natural operand order of v_mfma_f32_32x32x16_bf16: every lane
+// feeds 8 consecutive k of one A row and 8 consecutive k of one W row, so LDS
+// tiles are read with 16-byte loads and never transposed.
 //
-// Tiling: 256 threads (4 waves) per 128x128 output tile, each wave a 64x64
-// quadrant = 2x2 MFMA 32x32 blocks (64 fp32 accumulators per lane). K advances
-// in steps of 32 through a double-buffered LDS tile; the next tile's global
-// loads are in flight while the current one feeds the MFMAs.
-// fp32 A operands (the latent x and the condition features) are rounded to
-// bf16 while being staged, so no separate conversion pass touches HBM.
+// A block computes a BM x BN output tile with WGM x WGN waves; each wave owns a
+// (BM/WGM) x (BN/WGN) sub-tile made of 32x32 MFMA blocks. K is staged BK at a
+// time through two LDS buffers: the next stage's global loads are issued at the
+// top of an iteration and written to the other buffer at its end, and inside a
+// stage the fragments of k-step ks+1 are read from LDS while the MFMAs of
+// k-step ks run. LDS rows are padded by 16 bytes so the 16-byte fragment reads
+// of consecutive rows fall on distinct banks.
+//
+// Blocks are numbered so that the tiles one XCD runs at the same time share
+// operand rows in that XCD's L2: the hardware deals block ids round-robin to
+// the 8 XCDs, so each XCD's ids are mapped to a contiguous range of tile
+// numbers, and tiles are walked in groups of GROUP_M block-rows.
+//
+// fp32 A operands (latent x and condition features) are rounded to bf16 while
+// being staged, so no separate conversion pass touches HBM.
+#include <type_traits>
+
 #include "epilogue.h"
 
 namespace cfm {
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 32;
-constexpr int LDK = BK + 8;          // LDS row pitch in bf16 (80 B): spreads rows over banks
-constexpr int NT = 256;
+constexpr int PAD = 8;        // bf16 elements of padding per LDS row
+constexpr int GROUP_M = 4;
 
-template <typename AT> struct AStage;
+template <int BM_, int BN_, int BK_, int WGM_, int WGN_>
+struct Cfg {
+    static constexpr int BM = BM_, BN = BN_, BK = BK_, WGM = WGM_, WGN = WGN_;
+    static constexpr int NT = 64 * WGM * WGN;
+    static constexpr int WM = BM / WGM, WN = BN / WGN;         // wave sub-tile
+    static constexpr int TM = WM / 32, TN = WN / 32;           // MFMA blocks per wave
+    static constexpr int LDK = BK + PAD;
+    static constexpr int CPR = BK / 8;                         // 16-byte chunks per row
+    static constexpr int LDS_BYTES = 2 * (BM + BN) * LDK * 2;
+    static_assert(TM >= 1 && TN >= 1 && WM % 32 == 0 && WN % 32 == 0, "wave tile");
+    static_assert((BM * CPR) % NT == 0 && (BN * CPR) % NT == 0, "chunk split");
+};
 
-// bf16 A: 128 rows x 4 chunks of 8 = 512 chunks, 2 per thread
-template <> struct AStage<bf16> {
-    bf16x8 v[2];
-    __device__ __forceinline__ void load(const bf16* A, int lda, int M, int K, int m0, int k0, int tid) {
+// Raw buffer resource over [rows x ld] elements: loads outside it return 0, so
+// the staging loads below need no branches for ragged M, N or K edges (an
+// out-of-range chunk is given an offset past the end of the buffer).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* p, long long bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
+}
+constexpr int OOB = 0x7ffffff0;
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+template <int ROWS, int CPR, int NT, int LDK>
+struct Bf16Stage {
+    static constexpr int CHUNKS = ROWS * CPR / NT;
+    i32x4 v[CHUNKS];
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int ld, int rows_total, int K, int r0, int k0, int tid) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            int c = tid + i * NT, row = c >> 2, kc = (c & 3) * 8;
-            int m = m0 + row, k = k0 + kc;
-            if (m < M && k < K) v[i] = *(const bf16x8*)(A + (long long)m * lda + k);
-            else v[i] = bf16x8{};
+        for (int i = 0; i < CHUNKS; ++i) {
+            const int c = tid + i * NT, row = c / CPR, kc = (c % CPR) * 8;
+            const int r = r0 + row, k = k0 + kc;
+            const int off = (r < rows_total && k < K) ? (r * ld + k) * 2 : OOB;
+            v[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
         }
     }
-    __device__ __forceinline__ void store(bf16* As, int tid) const {
+    __device__ __forceinline__ void store(bf16* S, int tid) const {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            int c = tid + i * NT, row = c >> 2, kc = (c & 3) * 8;
-            *(bf16x8*)(As + row * LDK + kc) = v[i];
+        for (int i = 0; i < CHUNKS; ++i) {
+            const int c = tid + i * NT, row = c / CPR, kc = (c % CPR) * 8;
+            *(i32x4*)(S + row * LDK + kc) = v[i];
         }
     }
 };
 
-// fp32 A: 128 rows x 8 chunks of 4 = 1024 chunks, 4 per thread, rounded to bf16
-template <> struct AStage<float> {
-    f32x4 v[4];
-    __device__ __forceinline__ void load(const float* A, int lda, int M, int K, int m0, int k0, int tid) {
+// fp32 A operand: chunks of 4 floats, rounded to bf16 when written to LDS
+template <int ROWS, int BK, int NT, int LDK>
+struct F32Stage {
+    static constexpr int CPR = BK / 4;
+    static constexpr int CHUNKS = ROWS * CPR / NT;
+    i32x4 v[CHUNKS];
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int ld, int rows_total, int K, int r0, int k0, int tid) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            int c = tid + i * NT, row = c >> 3, kc = (c & 7) * 4;
-            int m = m0 + row, k = k0 + kc;
-            if (m < M && k < K) v[i] = *(const f32x4*)(A + (long long)m * lda + k);
-            else v[i] = f32x4{};
+        for (int i = 0; i < CHUNKS; ++i) {
+            const int c = tid + i * NT, row = c / CPR, kc = (c % CPR) * 4;
+            const int r = r0 + row, k = k0 + kc;
+            const int off = (r < rows_total && k < K) ? (r * ld + k) * 4 : OOB;
+            v[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
         }
     }
-    __device__ __forceinline__ void store(bf16* As, int tid) const {
+    __device__ __forceinline__ void store(bf16* S, int tid) const {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            int c = tid + i * NT, row = c >> 3, kc = (c & 7) * 4;
+        for (int i = 0; i < CHUNKS; ++i) {
+            const int c = tid + i * NT, row = c / CPR, kc = (c % CPR) * 4;
+            const f32x4 f = __builtin_bit_cast(f32x4, v[i]);
             bf16x4 b;
-            b[0] = (bf16)v[i][0]; b[1] = (bf16)v[i][1]; b[2] = (bf16)v[i][2]; b[3] = (bf16)v[i][3];
-            *(bf16x4*)(As + row * LDK + kc) = b;
+            b[0] = (bf16)f[0]; b[1] = (bf16)f[1]; b[2] = (bf16)f[2]; b[3] = (bf16)f[3];
+            *(bf16x4*)(S + row * LDK + kc) = b;
         }
     }
 };
 
-struct WStage {
-    bf16x8 v[2];
-    __device__ __forceinline__ void load(const bf16* W, int ldw, int N, int K, int n0, int k0, int tid) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            int c = tid + i * NT, row = c >> 2, kc = (c & 3) * 8;
-            int n = n0 + row, k = k0 + kc;
-            if (n < N && k < K) v[i] = *(const bf16x8*)(W + (long long)n * ldw + k);
-            else v[i] = bf16x8{};
-        }
-    }
-    __device__ __forceinline__ void store(bf16* Ws, int tid) const {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            int c = tid + i * NT, row = c >> 2, kc = (c & 3) * 8;
-            *(bf16x8*)(Ws + row * LDK + kc) = v[i];
-        }
-    }
-};
+template <typename AT, typename C> struct AStageOf { using type = Bf16Stage<C::BM, C::CPR, C::NT, C::LDK>; };
+template <typename C> struct AStageOf<float, C> { using type = F32Stage<C::BM, C::BK, C::NT, C::LDK>; };
 
-template <typename AT, int EPI>
-__global__ void __launch_bounds__(NT)
+__device__ __forceinline__ void tile_of(int bid, int nblocks, int tm, int tn, int& mt, int& nt) {
+    // XCD-major renumbering: XCD x runs the ids with id % 8 == x; give it a
+    // contiguous range of tile numbers (a bijection for any block count) ...
+    const int q = nblocks / 8, rem = nblocks % 8;
+    const int xcd = bid % 8, idx = bid / 8;
+    const int b = xcd * q + min(xcd, rem) + idx;
+    // ... then walk the tiles in groups of GROUP_M block-rows, column by column
+    const int group = GROUP_M * tn;
+    const int g = b / group, first_m = g * GROUP_M;
+    const int gm = min(tm - first_m, GROUP_M);
+    const int in = b - g * group;
+    mt = first_m + in % gm;
+    nt = in / gm;
+}
+
+template <typename C, typename AT, int EPI>
+__global__ void __launch_bounds__(C::NT)
 gemm_bf16_kernel(const AT* __restrict__ A, int lda, const bf16* __restrict__ W, int ldw,
-                 int M, int N, int K, EpiParams ep) {
-    __shared__ __attribute__((aligned(16))) bf16 As[2][BM * LDK];
-    __shared__ __attribute__((aligned(16))) bf16 Ws[2][BN * LDK];
+                 int M, int N, int K, int tm, int tn, EpiParams ep) {
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    bf16* const as_base = (bf16*)smem;                          // 2 stages of [BM][LDK]
+    bf16* const ws_base = (bf16*)smem + 2 * C::BM * C::LDK;     // 2 stages of [BN][LDK]
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int li = lane & 31, lh = lane >> 5;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
+    const int wm = wave / C::WGN, wn = wave % C::WGN;
+    int mt, nt;
+    tile_of(blockIdx.x, tm * tn, tm, tn, mt, nt);
+    const int m0 = mt * C::BM, n0 = nt * C::BN;
 
-    f32x16 acc[2][2];
+    f32x16 acc[C::TM][C::TN];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < C::TM; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+        for (int j = 0; j < C::TN; ++j) acc[i][j] = f32x16{};
 
-    AStage<AT> sa;
-    WStage sw;
-    const int nk = (K + BK - 1) / BK;
-    sa.load(A, lda, M, K, m0, 0, tid);
-    sw.load(W, ldw, N, K, n0, 0, tid);
-    sa.store(As[0], tid);
-    sw.store(Ws[0], tid);
+    typename AStageOf<AT, C>::type sa;
+    Bf16Stage<C::BN, C::CPR, C::NT, C::LDK> sw;
+    const __amdgpu_buffer_rsrc_t ra = rsrc_of(A, (long long)M * lda * sizeof(AT));
+    const __amdgpu_buffer_rsrc_t rw = rsrc_of(W, (long long)N * ldw * 2);
+    const int nk = (K + C::BK - 1) / C::BK;
+    sa.load(ra, lda, M, K, m0, 0, tid);
+    sw.load(rw, ldw, N, K, n0, 0, tid);
+    sa.store(as_base, tid);
+    sw.store(ws_base, tid);
     __syncthreads();
 
+    constexpr int KS = C::BK / 16;
     int cur = 0;
     for (int kt = 0; kt < nk; ++kt) {
         const bool more = kt + 1 < nk;
         if (more) {
-            sa.load(A, lda, M, K, m0, (kt + 1) * BK, tid);
-            sw.load(W, ldw, N, K, n0, (kt + 1) * BK, tid);
+            sa.load(ra, lda, M, K, m0, (kt + 1) * C::BK, tid);
+            sw.load(rw, ldw, N, K, n0, (kt + 1) * C::BK, tid);
         }
-        const bf16* as = As[cur];
-        const bf16* ws = Ws[cur];
+        const bf16* as = as_base + cur * C::BM * C::LDK + (wm * C::WM + li) * C::LDK + lh * 8;
+        const bf16* ws = ws_base + cur * C::BN * C::LDK + (wn * C::WN + li) * C::LDK + lh * 8;
+        bf16x8 a[2][C::TM], b[2][C::TN];
 #pragma unroll
-        for (int ks = 0; ks < BK / 16; ++ks) {
-            bf16x8 a[2], b[2];
+        for (int i = 0; i < C::TM; ++i) a[0][i] = *(const bf16x8*)(as + i * 32 * C::LDK);
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
-                a[i] = *(const bf16x8*)(as + (wm * 64 + i * 32 + li) * LDK + ks * 16 + lh * 8);
+        for (int j = 0; j < C::TN; ++j) b[0][j] = *(const bf16x8*)(ws + j * 32 * C::LDK);
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-                b[j] = *(const bf16x8*)(ws + (wn * 64 + j * 32 + li) * LDK + ks * 16 + lh * 8);
+        for (int ks = 0; ks < KS; ++ks) {
+            const int c = ks & 1;
+            if (ks + 1 < KS) {
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+                for (int i = 0; i < C::TM; ++i) a[c ^ 1][i] = *(const bf16x8*)(as + i * 32 * C::LDK + (ks + 1) * 16);
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+                for (int j = 0; j < C::TN; ++j) b[c ^ 1][j] = *(const bf16x8*)(ws + j * 32 * C::LDK + (ks + 1) * 16);
+            }
+#pragma unroll
+            for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+                for (int j = 0; j < C::TN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c][i], b[c][j], acc[i][j], 0, 0, 0);
         }
         if (more) {
-            sa.store(As[cur ^ 1], tid);
-            sw.store(Ws[cur ^ 1], tid);
+            sa.store(as_base + (cur ^ 1) * C::BM * C::LDK, tid);
+            sw.store(ws_base + (cur ^ 1) * C::BN * C::LDK, tid);
         }
         __syncthreads();
         cur ^= 1;
@@ -149,32 +194,74 @@ gemm_bf16_kernel(const AT* __restrict__ A, int lda, const bf16* __restrict__ W, 
     // accumulator layout of a 32x32 block: register g*4 + r holds
     // row 8g + 4*(lane/32) + r, column lane%32.
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < C::TM; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int n = n0 + wn * 64 + j * 32 + li;
+        for (int j = 0; j < C::TN; ++j) {
+            const int n = n0 + wn * C::WN + j * 32 + li;
             if (n >= N) continue;
 #pragma unroll
             for (int g = 0; g < 4; ++g)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int m = m0 + wm * 64 + i * 32 + 8 * g + 4 * lh + r;
+                    const int m = m0 + wm * C::WM + i * 32 + 8 * g + 4 * lh + r;
                     if (m < M) epi_store<EPI, bf16>(ep, m, n, acc[i][j][g * 4 + r]);
                 }
         }
 }
 
+template <typename C, typename AT, int EPI>
+void launch_cfg(const AT* A, int lda, const bf16* W, int ldw, int M, int N, int K,
+                const EpiParams& ep, hipStream_t s) {
+    const int tn = (N + C::BN - 1) / C::BN, tm = (M + C::BM - 1) / C::BM;
+    static const bool attr = [] {
+        return hipFuncSetAttribute((const void*)gemm_bf16_kernel<C, AT, EPI>,
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES) == hipSuccess;
+    }();
+    (void)attr;
+    gemm_bf16_kernel<C, AT, EPI><<<tm * tn, C::NT, C::LDS_BYTES, s>>>(A, lda, W, ldw, M, N, K, tm, tn, ep);
+}
+
+// tile configurations (index = the `tile` argument; 0 = automatic)
+using C1 = Cfg<128, 128, 32, 2, 2>;     // 4 waves, 64x64 per wave
+using C2 = Cfg<256, 256, 64, 2, 2>;     // 4 waves, 128x128 per wave
+using C3 = Cfg<256, 256, 32, 2, 4>;     // 8 waves, 128x64 per wave
+using C4 = Cfg<256, 128, 64, 2, 2>;     // 4 waves, 128x64 per wave
+using C5 = Cfg<256, 256, 64, 4, 2>;     // 8 waves, 64x128 per wave
+using C6 = Cfg<128, 128, 64, 2, 2>;     // 4 waves, 64x64 per wave, deeper K stage
+using CF = Cfg<128, 128, 32, 2, 2>;     // fp32 A operands
+
+template <typename AT, int EPI>
+void launch_epi(int tile, const AT* A, int lda, const bf16* W, int ldw, int M, int N, int K,
+                const EpiParams& ep, hipStream_t s) {
+    if constexpr (std::is_same<AT, float>::value) {
+        launch_cfg<CF, AT, EPI>(A, lda, W, ldw, M, N, K, ep, s);
+    } else {
+        if (tile == 0) {
+            // 256x256 tiles (8 waves) when they still give about one tile per CU or more
+            const long long big = (long long)((M + 255) / 256) * ((N + 255) / 256);
+            tile = big >= 192 ? 5 : 6;
+        }
+        switch (tile) {
+            case 2: launch_cfg<C2, AT, EPI>(A, lda, W, ldw, M, N, K, ep, s); break;
+            case 3: launch_cfg<C3, AT, EPI>(A, lda, W, ldw, M, N, K, ep, s); break;
+            case 4: launch_cfg<C4, AT, EPI>(A, lda, W, ldw, M, N, K, ep, s); break;
+            case 5: launch_cfg<C5, AT, EPI>(A, lda, W, ldw, M, N, K, ep, s); break;
+            case 6: launch_cfg<C6, AT, EPI>(A, lda, W, ldw, M, N, K, ep, s); break;
+            default: launch_cfg<C1, AT, EPI>(A, lda, W, ldw, M, N, K, ep, s); break;
+        }
+    }
+}
+
 template <typename AT>
-void launch_a(int epi, const AT* A, int lda, const bf16* W, int ldw, int M, int N, int K,
+void launch_a(int tile, int epi, const AT* A, int lda, const bf16* W, int ldw, int M, int N, int K,
               const EpiParams& ep, hipStream_t s) {
-    dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM);
     switch (epi) {
-        case EPI_F32: gemm_bf16_kernel<AT, EPI_F32><<<grid, NT, 0, s>>>(A, lda, W, ldw, M, N, K, ep); break;
-        case EPI_ACT: gemm_bf16_kernel<AT, EPI_ACT><<<grid, NT, 0, s>>>(A, lda, W, ldw, M, N, K, ep); break;
-        case EPI_GELU_ACT: gemm_bf16_kernel<AT, EPI_GELU_ACT><<<grid, NT, 0, s>>>(A, lda, W, ldw, M, N, K, ep); break;
-        case EPI_GATED: gemm_bf16_kernel<AT, EPI_GATED><<<grid, NT, 0, s>>>(A, lda, W, ldw, M, N, K, ep); break;
-        case EPI_INPROJ: gemm_bf16_kernel<AT, EPI_INPROJ><<<grid, NT, 0, s>>>(A, lda, W, ldw, M, N, K, ep); break;
-        case EPI_VOUT: gemm_bf16_kernel<AT, EPI_VOUT><<<grid, NT, 0, s>>>(A, lda, W, ldw, M, N, K, ep); break;
+        case EPI_F32: launch_epi<AT, EPI_F32>(tile, A, lda, W, ldw, M, N, K, ep, s); break;
+        case EPI_ACT: launch_epi<AT, EPI_ACT>(tile, A, lda, W, ldw, M, N, K, ep, s); break;
+        case EPI_GELU_ACT: launch_epi<AT, EPI_GELU_ACT>(tile, A, lda, W, ldw, M, N, K, ep, s); break;
+        case EPI_GATED: launch_epi<AT, EPI_GATED>(tile, A, lda, W, ldw, M, N, K, ep, s); break;
+        case EPI_INPROJ: launch_epi<AT, EPI_INPROJ>(tile, A, lda, W, ldw, M, N, K, ep, s); break;
+        case EPI_VOUT: launch_epi<AT, EPI_VOUT>(tile, A, lda, W, ldw, M, N, K, ep, s); break;
         default: break;
     }
 }
@@ -182,10 +269,10 @@ void launch_a(int epi, const AT* A, int lda, const bf16* W, int ldw, int M, int 
 }  // namespace
 
 void launch_gemm_bf16(bool a_f32, int epi, const void* A, int lda, const bf16* W, int ldw,
-                      int M, int N, int K, const EpiParams& ep, hipStream_t s) {
+                      int M, int N, int K, const EpiParams& ep, hipStream_t s, int tile) {
     if (M <= 0 || N <= 0) return;
-    if (a_f32) launch_a<float>(epi, (const float*)A, lda, W, ldw, M, N, K, ep, s);
-    else launch_a<bf16>(epi, (const bf16*)A, lda, W, ldw, M, N, K, ep, s);
+    if (a_f32) launch_a<float>(tile, epi, (const float*)A, lda, W, ldw, M, N, K, ep, s);
+    else launch_a<bf16>(tile, epi, (const bf16*)A, lda, W, ldw, M, N, K, ep, s);
 }
 
 }  // namespace cfm

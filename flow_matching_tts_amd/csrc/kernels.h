@@ -31,8 +31,9 @@ struct EpiParams {
 };
 
 // bf16 MFMA GEMM, A bf16 or f32 (rounded to bf16 while staging), W bf16 [N, K].
+// tile: 0 = pick by problem size, 1 = 128x128, 2 = 256x256 (bf16 A only)
 void launch_gemm_bf16(bool a_f32, int epi, const void* A, int lda, const bf16* W, int ldw,
-                      int M, int N, int K, const EpiParams& ep, hipStream_t s);
+                      int M, int N, int K, const EpiParams& ep, hipStream_t s, int tile = 0);
 // fp32 SIMT GEMM, A f32 (optionally SiLU on load), W f32 or bf16 [N, K]; EPI_ACT stores f32.
 void launch_gemm_simt(bool w_bf16, bool silu_a, int epi, const float* A, int lda, const void* W,
                       int ldw, int M, int N, int K, const EpiParams& ep, hipStream_t s);

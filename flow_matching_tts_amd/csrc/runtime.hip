@@ -16,6 +16,7 @@
 // weights are kernel arguments computed on the host (the vLLM-Omni blog's
 // "CFM/LocDiT decode-tail batching" section removes exactly such per-step
 // host syncs from its Euler loop).
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -43,6 +44,8 @@ cfm_status fail(cfm_status s, const char* fmt, ...) {
     return s;
 }
 
+constexpr long long kMaxOperandBytes = (1LL << 31) - 256;
+
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 inline long long round8(long long v) { return (v + 7) / 8 * 8; }
 
@@ -65,6 +68,18 @@ cfm_status check_config(const cfm_config* c) {
     if (c->spk_dim % 4) return fail(CFM_E_UNSUPPORTED, "spk_dim must be a multiple of 4");
     if (c->dtype == CFM_BF16 && hd != 64) return fail(CFM_E_UNSUPPORTED, "bf16 path needs head_dim 64 (got %d)", hd);
     if (c->dtype == CFM_F32 && (hd % 4 || hd > 64)) return fail(CFM_E_UNSUPPORTED, "fp32 path needs head_dim %% 4 == 0 and <= 64");
+    {
+        // the matrix-core GEMMs address each operand with 32-bit byte offsets
+        const long long es = c->dtype == CFM_BF16 ? 2 : 4;
+        const long long P = c->cond_mode == CFM_COND_PREFIX ? c->n_prefix : 0;
+        const long long tokens = (long long)c->n_branches * c->max_requests * (c->max_frames + P);
+        const long long wide = std::max<long long>(3LL * c->d_model, c->ffn_dim);
+        const long long cond_rows = (long long)c->max_requests * (P > 0 ? P : c->max_frames);
+        if (tokens * wide * es >= kMaxOperandBytes ||
+            (long long)c->max_requests * c->max_frames * c->latent_dim * 4 >= kMaxOperandBytes ||
+            cond_rows * std::max(c->cond_dim, c->latent_dim) * 4 >= kMaxOperandBytes)
+            return fail(CFM_E_UNSUPPORTED, "capacity too large: an activation operand would exceed 2 GiB");
+    }
     if (c->cond_mode == CFM_COND_PREFIX) {
         if (c->n_prefix <= 0) return fail(CFM_E_UNSUPPORTED, "prefix mode needs n_prefix > 0");
         if (c->cond_dim != c->latent_dim) return fail(CFM_E_UNSUPPORTED, "prefix mode needs cond_dim == latent_dim");
@@ -561,8 +576,9 @@ cfm_status cfm_cfg_euler(const float* v, const float* w, int nb, float dt, const
 
 cfm_status cfm_gemm_bf16(const void* A, int a_is_f32, int lda, const void* W, int ldw,
                          const float* bias, int M, int N, int K, int epilogue,
-                         const float* gate, void* C, int ldc, void* stream) {
+                         const float* gate, void* C, int ldc, int tile, void* stream) {
     if (M < 0 || N < 0 || K < 0) return fail(CFM_E_VALUE, "negative size");
+    if (tile < 0 || tile > 6 || (tile > 1 && a_is_f32)) return fail(CFM_E_VALUE, "tile %d", tile);
     if (epilogue < 0 || epilogue > 3) return fail(CFM_E_VALUE, "epilogue %d", epilogue);
     if (M == 0 || N == 0) return CFM_OK;
     if (A == nullptr || W == nullptr || C == nullptr) return fail(CFM_E_NULL, "A, W or C is NULL");
@@ -571,6 +587,8 @@ cfm_status cfm_gemm_bf16(const void* A, int a_is_f32, int lda, const void* W, in
     if (K % kq || lda % kq || ldw % 8 || lda < K || ldw < round8(K) || ldc < N)
         return fail(CFM_E_SHAPE, "K/lda/ldw/ldc do not meet the layout rules");
     if (!aligned16(A) || !aligned16(W)) return fail(CFM_E_SHAPE, "A and W must be 16-byte aligned");
+    if ((long long)M * lda * (a_is_f32 ? 4 : 2) >= kMaxOperandBytes || (long long)N * ldw * 2 >= kMaxOperandBytes)
+        return fail(CFM_E_SHAPE, "operand above 2 GiB");
     static const int map[4] = {EPI_F32, EPI_ACT, EPI_GELU_ACT, EPI_GATED};
     EpiParams ep;
     ep.bias = bias;
@@ -582,7 +600,8 @@ cfm_status cfm_gemm_bf16(const void* A, int a_is_f32, int lda, const void* W, in
     ep.gate.n_requests = 1;
     ep.gate.spk_branch = -1;
     (void)hipGetLastError();
-    launch_gemm_bf16(a_is_f32 != 0, map[epilogue], A, lda, (const bf16*)W, ldw, M, N, K, ep, (hipStream_t)stream);
+    launch_gemm_bf16(a_is_f32 != 0, map[epilogue], A, lda, (const bf16*)W, ldw, M, N, K, ep, (hipStream_t)stream,
+                     tile);
     hipError_t e = hipGetLastError();
     return e == hipSuccess ? CFM_OK : fail(CFM_E_HIP, "launch failed: %s", hipGetErrorString(e));
 }

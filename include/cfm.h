@@ -179,10 +179,12 @@ cfm_status cfm_cfg_euler(const float* v, const float* w, int nb, float dt, const
  *   [N] or NULL. epilogue 0: C fp32; 1: C bf16; 2: C bf16 of GELU(exact erf);
  *   3: gated residual C(fp32) += gate[n] * (acc + bias[n]) with gate device fp32 [N].
  * K % 8 == 0 (bf16 A) or K % 4 == 0 (fp32 A); lda, ldw multiples of 8 (bf16)
- * or 4 (fp32 A); ldw >= K rounded up to 8 with zero padding. */
+ * or 4 (fp32 A); ldw >= K rounded up to 8 with zero padding.
+ * tile: 0 = chosen from the problem size (what cfm_sample uses), 1 = 128x128
+ * output tiles, 2 = 256x256 output tiles (bf16 A only). */
 cfm_status cfm_gemm_bf16(const void* A, int a_is_f32, int lda, const void* W, int ldw,
                          const float* bias, int M, int N, int K, int epilogue,
-                         const float* gate, void* C, int ldc, void* stream);
+                         const float* gate, void* C, int ldc, int tile, void* stream);
 
 /* Key-padding-masked multi-head attention, bf16 in / bf16 out, fp32 softmax.
  *   qkv device bf16 [rows, T, 3 * H * 64] (q | k | v, head j at columns j*64)

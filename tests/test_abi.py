@@ -147,9 +147,10 @@ def test_single_kernel_entry_validation(lib):
     assert lib.cfm_cfg_euler(1 << 20, g, 2, C.c_float(0.1), None, 2, 3, 6, 1 << 21, None) == 2
     assert lib.cfm_cfg_euler(1 << 20, g, 4, C.c_float(0.1), None, 2, 3, 4, 1 << 21, None) == 4
     assert lib.cfm_cfg_euler(None, g, 2, C.c_float(0.1), None, 0, 3, 4, None, None) == 0
-    assert lib.cfm_gemm_bf16(1 << 20, 0, 12, 1 << 21, 16, None, 4, 4, 12, 0, None, 1 << 22, 4, None) == 2
-    assert lib.cfm_gemm_bf16(1 << 20, 0, 16, 1 << 21, 16, None, 4, 4, 16, 3, None, 1 << 22, 4, None) == 1
-    assert lib.cfm_gemm_bf16(1 << 20, 0, 16, 1 << 21, 16, None, 4, 4, 16, 9, None, 1 << 22, 4, None) == 4
+    assert lib.cfm_gemm_bf16(1 << 20, 0, 12, 1 << 21, 16, None, 4, 4, 12, 0, None, 1 << 22, 4, 0, None) == 2
+    assert lib.cfm_gemm_bf16(1 << 20, 0, 16, 1 << 21, 16, None, 4, 4, 16, 3, None, 1 << 22, 4, 0, None) == 1
+    assert lib.cfm_gemm_bf16(1 << 20, 0, 16, 1 << 21, 16, None, 4, 4, 16, 9, None, 1 << 22, 4, 0, None) == 4
+    assert lib.cfm_gemm_bf16(1 << 20, 1, 16, 1 << 21, 16, None, 4, 4, 16, 0, None, 1 << 22, 4, 2, None) == 4
     assert lib.cfm_attention_bf16(None, None, None, 2, 8, 1, None, None) == 1
     assert lib.cfm_attention_bf16(None, None, None, 0, 8, 1, None, None) == 0
     assert lib.cfm_adaln(1 << 20, 1 << 21, 1 << 22, 4, 30, 0, 1 << 23, None) == 2

@@ -83,9 +83,11 @@ def _gemm_ref(A, W, bias, epi, gate=None, c0=None):
     return c0.astype(np.float64) + gate.astype(np.float64) * acc
 
 
-@pytest.mark.parametrize("M,N,K", [(300, 200, 136), (128, 128, 64), (1, 3, 8), (1000, 100, 1024), (257, 3072, 1024)])
+@pytest.mark.parametrize("M,N,K", [(300, 200, 136), (128, 128, 64), (1, 3, 8), (1000, 100, 1024), (257, 3072, 1024),
+                                   (520, 600, 2048)])
 @pytest.mark.parametrize("epi", [0, 1, 2, 3])
-def test_gemm_bf16_epilogues(M, N, K, epi):
+@pytest.mark.parametrize("tile", [1, 2, 3, 4, 5, 6])
+def test_gemm_bf16_epilogues(M, N, K, epi, tile):
     import flow_matching_tts_amd as F
     rng = np.random.default_rng(M * 7 + N + K + epi)
     A = _bf(rng.standard_normal((M, K)))
@@ -98,7 +100,7 @@ def test_gemm_bf16_epilogues(M, N, K, epi):
     else:
         out = dev(c0 if epi == 3 else np.zeros((M, N), np.float32))
     F.gemm_bf16(dev(A, torch.bfloat16), dev(W, torch.bfloat16), dev(bias), epilogue=epi, out=out,
-                gate=dev(gate))
+                gate=dev(gate), tile=tile)
     got = out.float().cpu().numpy()
     want = _gemm_ref(A, W, bias, epi, gate, c0)
     if epi in (1, 2):      # bf16 output: within one bf16 rounding (2^-8 relative) of the fp64 value
