@@ -87,7 +87,7 @@ def load() -> C.CDLL:
     lib.cfm_cfg_euler.restype = i32
     lib.cfm_gemm_bf16.argtypes = [vp, i32, i32, vp, i32, vp, i32, i32, i32, i32, vp, vp, i32, i32, vp]
     lib.cfm_gemm_bf16.restype = i32
-    lib.cfm_attention_bf16.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp]
+    lib.cfm_attention_bf16.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp, C.c_size_t, vp, vp]
     lib.cfm_attention_bf16.restype = i32
     lib.cfm_adaln.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp]
     lib.cfm_adaln.restype = i32
@@ -242,10 +242,14 @@ def gemm_bf16(A, W, bias=None, *, epilogue: int, out, gate=None, K: Optional[int
     return out
 
 
-def attention_bf16(qkv, kv_len, o, *, n_heads: int, key_mask=None, stream=None):
-    rows, T = int(qkv.shape[0]), int(qkv.shape[1])
-    check(load().cfm_attention_bf16(_ptr(qkv), _ptr(kv_len), _ptr(key_mask), rows, T, int(n_heads),
-                                    _ptr(o), _stream(stream)))
+def attention_bf16(qk, vt, kv_len, o, *, n_heads: int, key_mask=None, stream=None):
+    """qk bf16 [rows, T, 2*H*64], vt bf16 [rows, H, 64, Tp] (Tp = T rounded up to 64)."""
+    import torch
+    rows, T = int(qk.shape[0]), int(qk.shape[1])
+    Tp = (T + 63) // 64 * 64
+    scratch = torch.empty(rows * 4 + rows * Tp + rows * (Tp // 64) + 64, dtype=torch.uint8, device=qk.device)
+    check(load().cfm_attention_bf16(_ptr(qk), _ptr(vt), _ptr(kv_len), _ptr(key_mask), rows, T,
+                                    int(n_heads), _ptr(scratch), scratch.numel(), _ptr(o), _stream(stream)))
     return o
 
 

@@ -1,9 +1,13 @@
 // Key-padding-masked multi-head attention over latent frames (non-causal).
 //
-// bf16 path (head_dim 64): flash-style, one block = 4 waves = 128 queries of
-// one (row, head); keys stream through LDS in tiles of 64 with the online
-// softmax recurrence (running max m, running sum l, rescale of the partial
-// output by exp(m_old - m_new)), so the T x T score matrix never exists.
+// bf16 path (head_dim 64): flash-style, one block = 8 waves = 256 queries of
+// one (row, head), 32 per wave, all sharing each K and V^T tile staged in LDS;
+// keys stream through double-buffered LDS tiles
+// of 64 with the online softmax recurrence (running max m, running sum l,
+// rescale of the partial output by exp(m_old - m_new)), so the T x T score
+// matrix never exists. V arrives already transposed per head (the QKV GEMM
+// epilogue writes it that way), so every LDS tile is filled with plain
+// 16-byte loads and stores.
 //
 // MFMA mapping (v_mfma_f32_32x32x16_bf16, C[i][j] = sum_k A[i][k] B[k][j]):
 //   S^T = K Q^T : A = the K tile (rows = keys), B = Q^T held in registers for
@@ -15,8 +19,13 @@
 //                 query per lane); the k slots of that operand are a fixed
 //                 permutation of the tile's keys, and the V^T operand is read
 //                 from LDS in that same key order.
+// Occupancy is what hides latency here: the kernel is limited to 128 VGPRs so
+// that two 8-wave blocks share a CU (4 waves per SIMD), and tiles alternate
+// between two LDS buffers so one barrier per tile suffices.
 // Masked keys are zero-filled in K and V and get a -inf score bias, so a
-// non-finite value behind a padded frame can never reach a valid output.
+// non-finite value behind a padded frame can never reach a valid output; tiles
+// whose 64 keys are all valid skip the bias. The 1/sqrt(hd) scale is folded into
+// the exp2 argument, and the running max moves lazily (see RESCALE_SLACK).
 //
 // fp32 path: one thread per query, exact fp32 online softmax, for the fp32
 // sampler (small head dims).
@@ -27,10 +36,17 @@ namespace cfm {
 namespace {
 
 constexpr int HD = 64;
-constexpr int QT = 128;        // queries per block
+constexpr int NW = 8;          // waves per block, 32 queries each
+constexpr int QT = 32 * NW;    // queries per block (they share every K / V^T tile)
+constexpr int NT = 64 * NW;
 constexpr int KT = 64;         // keys per LDS tile
 constexpr int KP = HD + 8;     // K tile row pitch (bf16): 144 B
 constexpr int VP = KT + 8;     // V^T tile row pitch (bf16): 144 B
+// The running max is only moved when a tile's max exceeds it by more than
+// 2^8 in probability (8 in base-2 exponent): until then p = 2^(s - m) <= 256,
+// far from overflow in fp32 and in bf16, and softmax does not depend on the
+// constant subtracted, so skipping the rescale changes nothing but rounding.
+constexpr float RESCALE_SLACK = 8.0f;
 
 __device__ __forceinline__ bool key_valid(const AttnParams& p, const uint8_t* km, int key, int kvl) {
     if (key >= kvl) return false;
@@ -38,77 +54,125 @@ __device__ __forceinline__ bool key_valid(const AttnParams& p, const uint8_t* km
     return km[key - p.P] != 0;
 }
 
-__global__ void __launch_bounds__(256)
+// One KV tile in registers on its way to LDS: KV_CH chunks of K (one key, 8
+// head dims each) and of V^T (one head dim, 8 keys each) per thread, with the
+// validity bytes of their keys. Masked keys are written as zeros.
+constexpr int KV_CH = KT * HD / 8 / NT;
+static_assert(KV_CH >= 1 && KT * HD / 8 % NT == 0, "tile split");
+struct KvStage {
+    bf16x8 k[KV_CH], v[KV_CH];
+    uint8_t kok[KV_CH];
+    uint64_t vok[KV_CH];
+    __device__ __forceinline__ void load(const bf16* kbase, long long ldk, int kmax, const bf16* vtbase,
+                                         int Tp, const uint8_t* kv, int k0, int tid) {
+#pragma unroll
+        for (int i = 0; i < KV_CH; ++i) {
+            const int c = tid + i * NT;
+            const int key = k0 + (c >> 3), ch = (c & 7) * 8;
+            kok[i] = kv[key];
+            k[i] = *(const bf16x8*)(kbase + (long long)min(key, kmax) * ldk + ch);
+            const int hd = c >> 3, kc = k0 + (c & 7) * 8;
+            vok[i] = *(const uint64_t*)(kv + kc);
+            v[i] = *(const bf16x8*)(vtbase + (long long)hd * Tp + kc);
+        }
+    }
+    __device__ __forceinline__ void store(bf16* Ks, bf16* Vt, float* kbias, int tid) const {
+#pragma unroll
+        for (int i = 0; i < KV_CH; ++i) {
+            const int c = tid + i * NT;
+            const int kr = c >> 3, ch = (c & 7) * 8;
+            *(bf16x8*)(Ks + kr * KP + ch) = kok[i] ? k[i] : bf16x8{};
+            if (ch == 0) kbias[kr] = kok[i] ? 0.0f : -INFINITY;
+            const int hd = c >> 3, kc = (c & 7) * 8;
+            bf16x8 vv = v[i];
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (((vok[i] >> (8 * e)) & 0xff) == 0) vv[e] = (bf16)0.0f;
+            *(bf16x8*)(Vt + hd * VP + kc) = vv;
+        }
+    }
+};
+
+__global__ void __launch_bounds__(NT, 4)   // 4 waves per SIMD: two blocks per CU
 attn_bf16_kernel(AttnParams p) {
-    __shared__ __attribute__((aligned(16))) bf16 Ks[KT * KP];
-    __shared__ __attribute__((aligned(16))) bf16 Vt[HD * VP];
-    __shared__ float kbias[KT];
+    __shared__ __attribute__((aligned(16))) bf16 Ks[2][KT * KP];
+    __shared__ __attribute__((aligned(16))) bf16 Vt[2][HD * VP];
+    __shared__ float kbias[2][KT];
 
     const int row = blockIdx.z, head = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int j = lane & 31, h = lane >> 5;
     const int T = p.T, d = p.H * HD;
-    const long long ld = 3LL * d;
-    const bf16* base = (const bf16*)p.qkv + (long long)row * T * ld;
+    const long long ldk = 2LL * d;
+    const bf16* qbase = (const bf16*)p.qkv + (long long)row * T * ldk + head * HD;
+    const bf16* kbase = qbase + d;
+    const bf16* vtbase = (const bf16*)p.vt + (long long)(row * p.H + head) * HD * p.Tp;
     const int q = blockIdx.x * QT + wave * 32 + j;
 
     bf16x8 qf[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
-        qf[kk] = q < T ? *(const bf16x8*)(base + (long long)q * ld + head * HD + kk * 16 + h * 8) : bf16x8{};
+        qf[kk] = q < T ? *(const bf16x8*)(qbase + (long long)q * ldk + kk * 16 + h * 8) : bf16x8{};
 
     const int rr = row % p.kv_mod;
     const int kvl = min(p.kv_len[rr], T);
-    const uint8_t* km = p.key_mask ? p.key_mask + (long long)rr * p.mask_stride : nullptr;
+    const uint8_t* kv = p.kvalid + (long long)rr * p.Tp;
+    const uint8_t* tfull = p.tile_full + (long long)rr * (p.Tp / KT);
     const float sl2 = 1.4426950408889634f / sqrtf((float)HD);   // 1/sqrt(hd) in base-2 units
 
     f32x16 oacc[2] = {f32x16{}, f32x16{}};
-    float m_run = -1e30f, l_part = 0.0f;
+    // running max of the scaled scores (base 2); finite start so that a tile with
+    // no valid key (all scores -inf) gives exp2(-inf) = 0, never inf - inf
+    float m_run = -1e30f;
+    float l_part = 0.0f;
 
-    for (int k0 = 0; k0 < kvl; k0 += KT) {
-#pragma unroll
-        for (int pass = 0; pass < 2; ++pass) {
-            const int c = tid + pass * 256, key = c >> 3, ch = (c & 7) * 8;
-            const int kg = k0 + key;
-            const bool ok = key_valid(p, km, kg, kvl);
-            bf16x8 kv = bf16x8{}, vv = bf16x8{};
-            if (ok) {
-                const bf16* src = base + (long long)kg * ld + head * HD + ch;
-                kv = *(const bf16x8*)(src + d);
-                vv = *(const bf16x8*)(src + 2 * d);
-            }
-            *(bf16x8*)(Ks + key * KP + ch) = kv;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) Vt[(ch + e) * VP + key] = vv[e];
-            if (ch == 0) kbias[key] = ok ? 0.0f : -INFINITY;
+    const int ntiles = (kvl + KT - 1) / KT;
+    for (int it = 0; it < ntiles; ++it) {
+        const int cur = it & 1;
+        const bool full = tfull[it] != 0;
+        {
+            KvStage st;
+            st.load(kbase, ldk, T - 1, vtbase, p.Tp, kv, it * KT, tid);
+            st.store(Ks[cur], Vt[cur], kbias[cur], tid);
         }
         __syncthreads();
+        const bf16* ks = Ks[cur];
+        const bf16* vt = Vt[cur];
 
-        f32x16 s[2];
+        // S^T = K Q^T: s[kh][g*4 + r] = score(key kh*32 + 8g + 4h + r, query q)
+        f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-            s[kh] = f32x16{};
+        for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
-                const bf16x8 a = *(const bf16x8*)(Ks + (kh * 32 + j) * KP + kk * 16 + h * 8);
+                const bf16x8 a = *(const bf16x8*)(ks + (kh * 32 + j) * KP + kk * 16 + h * 8);
                 s[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[kh], 0, 0, 0);
             }
+        if (!full) {   // partial tile: masked keys get -inf
+            const float* kb = kbias[cur];
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) s[kh][g * 4 + r] += kb[kh * 32 + 8 * g + 4 * h + r];
         }
-        // s[kh][g*4 + r] = score(key = kh*32 + 8g + 4h + r, query q)
         float mx = -INFINITY;
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-            for (int g = 0; g < 4; ++g)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float v = s[kh][g * 4 + r] * sl2 + kbias[kh * 32 + 8 * g + 4 * h + r];
-                    s[kh][g * 4 + r] = v;
-                    mx = fmaxf(mx, v);
-                }
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = exp2f(m_run - m_new);
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kh][i]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sl2;
+        // move the running max only when the tile max clears it by the slack
+        const bool move = mx > m_run + RESCALE_SLACK;
+        if (__any(move)) {   // some lane of the wave moves its max
+            const float m_new = move ? mx : m_run;
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 1 for lanes that keep their max
+            l_part *= alpha;
+            oacc[0] *= alpha;
+            oacc[1] *= alpha;
+            m_run = m_new;
+        }
         float ls = 0.0f;
         bf16x8 pb[2][2];
 #pragma unroll
@@ -117,32 +181,31 @@ attn_bf16_kernel(AttnParams p) {
             for (int g = 0; g < 4; ++g)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float pv = exp2f(s[kh][g * 4 + r] - m_new);
+                    const float pv = __builtin_amdgcn_exp2f(fmaf(s[kh][g * 4 + r], sl2, -m_run));
                     ls += pv;
                     pb[kh][g >> 1][(g & 1) * 4 + r] = (bf16)pv;
                 }
-        l_part = l_part * alpha + ls;
-        m_run = m_new;
-#pragma unroll
-        for (int dt = 0; dt < 2; ++dt) oacc[dt] *= alpha;
+        l_part += ls;
 
-        // B operand slot e of lane half h (k-step st of key half kh) is key
-        // kh*32 + 16 st + 4h + e for e < 4 and kh*32 + 16 st + 8 + 4h + (e - 4) for e >= 4.
+        // O^T += V^T P^T. B-operand slot e of lane half h (k-step ss of key half kh)
+        // is key kh*32 + 16 ss + 4h + e (e < 4) or kh*32 + 16 ss + 8 + 4h + (e - 4).
 #pragma unroll
         for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
             for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-                for (int st = 0; st < 2; ++st) {
-                    const bf16* vr = Vt + (dt * 32 + j) * VP + kh * 32 + 16 * st + 4 * h;
+                for (int ss = 0; ss < 2; ++ss) {
+                    const bf16* vr = vt + (dt * 32 + j) * VP + kh * 32 + 16 * ss + 4 * h;
                     const bf16x4 lo = *(const bf16x4*)(vr);
                     const bf16x4 hi = *(const bf16x4*)(vr + 8);
                     bf16x8 a;
                     a[0] = lo[0]; a[1] = lo[1]; a[2] = lo[2]; a[3] = lo[3];
                     a[4] = hi[0]; a[5] = hi[1]; a[6] = hi[2]; a[7] = hi[3];
-                    oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kh][st], oacc[dt], 0, 0, 0);
+                    oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kh][ss], oacc[dt], 0, 0, 0);
                 }
-        __syncthreads();
+
+        // no barrier here: the next tile goes to the other buffer, and the barrier
+        // after that store orders it after every wave's reads of this one
     }
 
     const float l = l_part + __shfl_xor(l_part, 32, 64);
@@ -216,7 +279,7 @@ attn_f32_kernel(AttnParams p) {
 void launch_attention_bf16(const AttnParams& p, hipStream_t s) {
     if (p.rows <= 0 || p.T <= 0) return;
     dim3 grid((p.T + QT - 1) / QT, p.H, p.rows);
-    attn_bf16_kernel<<<grid, 256, 0, s>>>(p);
+    attn_bf16_kernel<<<grid, NT, 0, s>>>(p);
 }
 
 void launch_attention_f32(const AttnParams& p, hipStream_t s) {

@@ -98,18 +98,38 @@ __global__ void timestep_embedding_kernel(float* temb, int S, int F) {
     temb[(long long)k * F + i] = (float)(i < half ? cos(arg) : sin(arg));
 }
 
-// kv_len[r] = P + 1 + index of the last valid frame of request r (P if none).
-__global__ void kv_len_kernel(const uint8_t* mask, int Tx, int P, int32_t* kv_len) {
-    __shared__ int best;
+// Per-request key validity (see launch_key_prep). One block per request.
+__global__ void key_prep_kernel(const uint8_t* mask, int mask_stride, const int32_t* kv_len_in, int P,
+                                int T, int Tp, int32_t* kv_len_out, uint8_t* kvalid, uint8_t* tile_full) {
+    __shared__ int last;
     const int r = blockIdx.x;
-    if (threadIdx.x == 0) best = 0;
+    const int Tx = T - P;
+    if (threadIdx.x == 0) last = 0;
     __syncthreads();
-    int mine = 0;
-    for (int t = threadIdx.x; t < Tx; t += blockDim.x)
-        if (mask == nullptr || mask[(long long)r * Tx + t]) mine = t + 1;
-    atomicMax(&best, mine);
+    int kvl;
+    if (kv_len_in != nullptr) {
+        kvl = min(max(kv_len_in[r], 0), T);
+    } else {
+        int mine = 0;
+        for (int t = threadIdx.x; t < Tx; t += blockDim.x)
+            if (mask == nullptr || mask[(long long)r * mask_stride + t]) mine = t + 1;
+        atomicMax(&last, mine);
+        __syncthreads();
+        kvl = P + last;
+    }
+    uint8_t* kv = kvalid + (long long)r * Tp;
+    for (int t = threadIdx.x; t < Tp; t += blockDim.x) {
+        bool ok = t < kvl;
+        if (ok && mask != nullptr && t >= P) ok = mask[(long long)r * mask_stride + (t - P)] != 0;
+        kv[t] = ok ? 1 : 0;
+    }
     __syncthreads();
-    if (threadIdx.x == 0) kv_len[r] = P + best;
+    for (int i = threadIdx.x; i < Tp / 64; i += blockDim.x) {
+        int all = 1;
+        for (int e = 0; e < 64; ++e) all &= kv[i * 64 + e];
+        tile_full[(long long)r * (Tp / 64) + i] = (uint8_t)all;
+    }
+    if (threadIdx.x == 0) kv_len_out[r] = kvl;
 }
 
 __global__ void assemble_cvec_kernel(const float* ct, const float* bs, const float* spkproj,
@@ -156,9 +176,11 @@ void launch_timestep_embedding(float* temb, int S, int F, hipStream_t s) {
     timestep_embedding_kernel<<<dim3((F + 127) / 128, S), 128, 0, s>>>(temb, S, F);
 }
 
-void launch_kv_len(const uint8_t* mask, int R, int Tx, int P, int32_t* kv_len, hipStream_t s) {
+void launch_key_prep(const uint8_t* mask, int mask_stride, const int32_t* kv_len_in, int R, int P,
+                     int T, int Tp, int32_t* kv_len_out, uint8_t* kvalid, uint8_t* tile_full,
+                     hipStream_t s) {
     if (R <= 0) return;
-    kv_len_kernel<<<R, 256, 0, s>>>(mask, Tx, P, kv_len);
+    key_prep_kernel<<<R, 256, 0, s>>>(mask, mask_stride, kv_len_in, P, T, Tp, kv_len_out, kvalid, tile_full);
 }
 
 void launch_assemble_cvec(const float* ct, const float* bs, const float* spkproj, int S, int nc,

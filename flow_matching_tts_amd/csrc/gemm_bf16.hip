@@ -200,12 +200,12 @@ gemm_bf16_kernel(const AT* __restrict__ A, int lda, const bf16* __restrict__ W, 
             const int n = n0 + wn * C::WN + j * 32 + li;
             if (n >= N) continue;
 #pragma unroll
-            for (int g = 0; g < 4; ++g)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int m = m0 + wm * C::WM + i * 32 + 8 * g + 4 * lh + r;
-                    if (m < M) epi_store<EPI, bf16>(ep, m, n, acc[i][j][g * 4 + r]);
-                }
+            for (int g = 0; g < 4; ++g) {
+                const int m = m0 + wm * C::WM + i * 32 + 8 * g + 4 * lh;
+                const float a4[4] = {acc[i][j][g * 4 + 0], acc[i][j][g * 4 + 1], acc[i][j][g * 4 + 2],
+                                     acc[i][j][g * 4 + 3]};
+                epi_store4<EPI, bf16>(ep, m, M, n, a4);
+            }
         }
 }
 
@@ -262,6 +262,7 @@ void launch_a(int tile, int epi, const AT* A, int lda, const bf16* W, int ldw, i
         case EPI_GATED: launch_epi<AT, EPI_GATED>(tile, A, lda, W, ldw, M, N, K, ep, s); break;
         case EPI_INPROJ: launch_epi<AT, EPI_INPROJ>(tile, A, lda, W, ldw, M, N, K, ep, s); break;
         case EPI_VOUT: launch_epi<AT, EPI_VOUT>(tile, A, lda, W, ldw, M, N, K, ep, s); break;
+        case EPI_QKV: launch_epi<AT, EPI_QKV>(tile, A, lda, W, ldw, M, N, K, ep, s); break;
         default: break;
     }
 }

@@ -14,6 +14,7 @@ enum Epi {
     EPI_GATED = 3,     // out f32 [m, n] += gate(m)[n] * (acc + bias)
     EPI_INPROJ = 4,    // input projection of latent token m = r*Tx + t into every branch row
     EPI_VOUT = 5,      // velocity: out f32 [m, n] = frame valid ? acc + bias : 0
+    EPI_QKV = 6,       // q|k columns -> out bf16 [m, 2d]; v columns -> vt bf16 [row, head, hd, Tp] (transposed)
 };
 
 struct EpiParams {
@@ -28,6 +29,10 @@ struct EpiParams {
     const float* cproj = nullptr;
     // EPI_VOUT: m = row*Tx + t, request r = row % R, mask [R, Tx] or null
     const uint8_t* mask = nullptr;
+    // EPI_QKV: token m = row*T + t; value column n - 2d of head hh = (n-2d)/64 lands at
+    // vt[((row*H + hh)*64 + (n-2d)%64)*Tp + t]; q and k columns go to out with row stride ldo (= 2d)
+    bf16* vt = nullptr;
+    int H = 0, Tp = 0, d2 = 0;
 };
 
 // bf16 MFMA GEMM, A bf16 or f32 (rounded to bf16 while staging), W bf16 [N, K].
@@ -39,7 +44,9 @@ void launch_gemm_simt(bool w_bf16, bool silu_a, int epi, const float* A, int lda
                       int ldw, int M, int N, int K, const EpiParams& ep, hipStream_t s);
 
 struct AttnParams {
-    const void* qkv;          // [rows, T, 3d]
+    const void* qkv;          // fp32 path: [rows, T, 3d]; bf16 path: q|k [rows, T, 2d]
+    const void* vt;           // bf16 path: V transposed per head [rows, H, 64, Tp]
+    int Tp;                   // padded key count of vt (multiple of 64)
     void* o;                  // [rows, T, d]
     int rows, T, H, hd;
     const int32_t* kv_len;    // per (row % kv_mod): keys >= kv_len are masked
@@ -47,6 +54,10 @@ struct AttnParams {
     const uint8_t* key_mask;  // [(row % kv_mod), Tm] for keys >= P, or null
     int mask_stride;          // Tm
     int P;                    // keys < P are always valid (condition prefix)
+    // bf16 path: per-key validity bytes [(row % kv_mod), Tp] and per-64-key-tile
+    // "all valid" bytes [(row % kv_mod), Tp / 64], made by launch_key_prep
+    const uint8_t* kvalid;
+    const uint8_t* tile_full;
 };
 void launch_attention_bf16(const AttnParams& p, hipStream_t s);
 void launch_attention_f32(const AttnParams& p, hipStream_t s);
@@ -67,8 +78,14 @@ void launch_cfg_euler(const float* v, int nb, float w0, float w1, float w2, cons
                       int R, int Tx, int C, float* x, hipStream_t s);
 // temb [S, F] = sinusoidal embedding of t_k = k / S (phase in fp64)
 void launch_timestep_embedding(float* temb, int S, int F, hipStream_t s);
-// kv_len[r] = P + (index of last valid frame of request r) + 1
-void launch_kv_len(const uint8_t* mask, int R, int Tx, int P, int32_t* kv_len, hipStream_t s);
+// Key validity of every request's sequence (P prefix keys, then Tx = T - P frames):
+// kv_len_out[r] = min(kv_len_in[r], T) if kv_len_in is given, else P + 1 + the
+// index of the last valid frame (P if none); kvalid[r, t] = t < kv_len_out[r] and
+// (t < P or mask[r, t - P] != 0 or no mask), zero for t in [T, Tp); tile_full[r, i]
+// = 1 when keys 64i .. 64i+63 are all valid.
+void launch_key_prep(const uint8_t* mask, int mask_stride, const int32_t* kv_len_in, int R, int P,
+                     int T, int Tp, int32_t* kv_len_out, uint8_t* kvalid, uint8_t* tile_full,
+                     hipStream_t s);
 // cvec[(k*nc + ci), :] = ct[k, :] + (spk ? (ci == 0 ? bs : spkproj[ci-1]) : 0)
 void launch_assemble_cvec(const float* ct, const float* bs, const float* spkproj, int S, int nc,
                           int d, float* cvec, hipStream_t s);

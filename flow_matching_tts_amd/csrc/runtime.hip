@@ -169,8 +169,10 @@ Slot find(const Manifest& m, const char* name, long long col0 = 0) {
 }
 
 struct Layout {   // workspace regions, byte offsets
-    size_t h, act, big, v, cproj, temb, tpre, ct, spkproj, cvec, mod, kvlen, total;
+    size_t h, act, big, vt, v, cproj, temb, tpre, ct, spkproj, cvec, mod, kvlen, kvalid, tfull, total;
 };
+
+inline long long round64(long long v) { return (v + 63) / 64 * 64; }
 
 Layout plan_workspace(const cfm_config& c) {
     const size_t es = c.dtype == CFM_BF16 ? 2 : 4;
@@ -187,6 +189,8 @@ Layout plan_workspace(const cfm_config& c) {
     L.h = take(N * T * d * 4);
     L.act = take(N * T * d * es);
     L.big = take(N * T * wide * es);
+    // bf16 path: V transposed per head, [rows, H, 64, T rounded up to 64]
+    L.vt = take(c.dtype == CFM_BF16 ? N * d * (size_t)round64(T) * 2 : 0);
     L.v = take(N * Tx * c.latent_dim * 4);
     L.cproj = take(Rm * Tc * d * 4);
     L.temb = take(S * c.t_freq_dim * 4);
@@ -196,6 +200,8 @@ Layout plan_workspace(const cfm_config& c) {
     L.cvec = take(S * nc * d * 4);
     L.mod = take(S * nc * ML * 4);
     L.kvlen = take(Rm * 4);
+    L.kvalid = take(Rm * (size_t)round64(T));           // per-key validity bytes
+    L.tfull = take(Rm * (size_t)round64(T) / 64);       // per-64-key-tile "all valid" bytes
     L.total = off;
     return L;
 }
@@ -430,6 +436,8 @@ cfm_status cfm_sample(cfm_ctx* c, const float* x0, const float* cond, const floa
     float* h = wsp<float>(c, ly.h);
     void* act = c->ws + ly.act;
     void* big = c->ws + ly.big;
+    bf16* vt = (bf16*)(c->ws + ly.vt);
+    const int Tp = (int)round64(T);
     float* vel = wsp<float>(c, ly.v);
     float* cproj = wsp<float>(c, ly.cproj);
     float* temb = wsp<float>(c, ly.temb);
@@ -439,6 +447,8 @@ cfm_status cfm_sample(cfm_ctx* c, const float* x0, const float* cond, const floa
     float* cvec = wsp<float>(c, ly.cvec);
     float* mod = wsp<float>(c, ly.mod);
     int32_t* kvlen = wsp<int32_t>(c, ly.kvlen);
+    uint8_t* kvalid = wsp<uint8_t>(c, ly.kvalid);
+    uint8_t* tfull = wsp<uint8_t>(c, ly.tfull);
 
     // GEMM through matrix cores (bf16 sampler) or fp32 FMA (fp32 sampler)
     auto gemm = [&](int cls, bool a_f32, const void* A, int lda, Slot w, int M, int Nn, int K, int epi,
@@ -461,7 +471,9 @@ cfm_status cfm_sample(cfm_ctx* c, const float* x0, const float* cond, const floa
     };
 
     // ---- set-up, once per call
-    timed(c, CFM_K_HOISTED, s, [&] { launch_kv_len(frame_mask, R, Tx, P, kvlen, s); });
+    timed(c, CFM_K_HOISTED, s, [&] {
+        launch_key_prep(frame_mask, Tx, nullptr, R, P, T, Tp, kvlen, kvalid, tfull, s);
+    });
     timed(c, CFM_K_HOISTED, s, [&] { launch_timestep_embedding(temb, S, g.t_freq_dim, s); });
     hoisted(false, temb, g.t_freq_dim, c->t1w, c->t1b, S, d, g.t_freq_dim, tpre, d);
     hoisted(true, tpre, d, c->t2w, c->t2b, S, d, d, ct, d);
@@ -493,8 +505,9 @@ cfm_status cfm_sample(cfm_ctx* c, const float* x0, const float* cond, const floa
     if (nb == 3) { w[0] = 1.0f - scales[0]; w[1] = scales[0] - scales[1]; w[2] = scales[1]; }
 
     AttnParams ap;
-    ap.qkv = big; ap.o = act; ap.rows = N; ap.T = T; ap.H = H; ap.hd = hd;
+    ap.qkv = big; ap.vt = vt; ap.Tp = Tp; ap.o = act; ap.rows = N; ap.T = T; ap.H = H; ap.hd = hd;
     ap.kv_len = kvlen; ap.kv_mod = R; ap.key_mask = frame_mask; ap.mask_stride = Tx; ap.P = P;
+    ap.kvalid = kvalid; ap.tile_full = tfull;
 
     // ---- Euler steps
     for (int k = 0; k < S; ++k) {
@@ -520,8 +533,13 @@ cfm_status cfm_sample(cfm_ctx* c, const float* x0, const float* cond, const floa
             ln.h = h; ln.y = act; ln.d = d; ln.n_out = NT; ln.Tin = T; ln.Tout = T; ln.off = 0;
             ln.shift = rowmod(ml + 0 * d, T); ln.scale = rowmod(ml + 1 * d, T); ln.out_bf16 = bf;
             timed(c, CFM_K_ADALN, s, [&] { launch_adaln(ln, s); });
-            EpiParams e1; e1.bias = wp<float>(c, W.qkvb); e1.out = big; e1.ldo = 3 * d;
-            gemm(CFM_K_GEMM_QKV, false, act, d, W.qkvw, (int)NT, 3 * d, d, EPI_ACT, e1);
+            EpiParams e1; e1.bias = wp<float>(c, W.qkvb); e1.out = big;
+            if (bf) {   // q|k rows of 2d, v transposed per head for the attention tiles
+                e1.ldo = 2 * d; e1.vt = vt; e1.H = H; e1.T = T; e1.Tp = Tp; e1.d2 = 2 * d;
+            } else {
+                e1.ldo = 3 * d;
+            }
+            gemm(CFM_K_GEMM_QKV, false, act, d, W.qkvw, (int)NT, 3 * d, d, bf ? EPI_QKV : EPI_ACT, e1);
             timed(c, CFM_K_ATTENTION, s, [&] {
                 if (bf) launch_attention_bf16(ap, s); else launch_attention_f32(ap, s);
             });
@@ -606,17 +624,28 @@ cfm_status cfm_gemm_bf16(const void* A, int a_is_f32, int lda, const void* W, in
     return e == hipSuccess ? CFM_OK : fail(CFM_E_HIP, "launch failed: %s", hipGetErrorString(e));
 }
 
-cfm_status cfm_attention_bf16(const void* qkv, const int32_t* kv_len, const uint8_t* key_mask,
-                              int rows, int T, int H, void* o, void* stream) {
+cfm_status cfm_attention_bf16(const void* qk, const void* vt, const int32_t* kv_len,
+                              const uint8_t* key_mask, int rows, int T, int H, void* scratch,
+                              size_t scratch_bytes, void* o, void* stream) {
     if (rows < 0 || T < 0 || H <= 0) return fail(CFM_E_VALUE, "bad rows/T/H");
     if (rows > 65535 || H > 65535) return fail(CFM_E_SHAPE, "rows and H must be <= 65535");
     if (rows == 0 || T == 0) return CFM_OK;
-    if (qkv == nullptr || kv_len == nullptr || o == nullptr) return fail(CFM_E_NULL, "qkv, kv_len or o is NULL");
-    if (!aligned16(qkv) || ((uintptr_t)o & 7)) return fail(CFM_E_SHAPE, "qkv 16-byte / o 8-byte alignment");
+    if (qk == nullptr || vt == nullptr || kv_len == nullptr || o == nullptr || scratch == nullptr)
+        return fail(CFM_E_NULL, "qk, vt, kv_len, scratch or o is NULL");
+    if (!aligned16(qk) || !aligned16(vt) || ((uintptr_t)o & 7) || ((uintptr_t)scratch & 15))
+        return fail(CFM_E_SHAPE, "qk, vt, scratch 16-byte / o 8-byte alignment");
+    const long long Tp = round64(T);
+    const size_t need = (size_t)rows * 4 + (size_t)rows * Tp + (size_t)rows * (Tp / 64) + 64;
+    if (scratch_bytes < need) return fail(CFM_E_WORKSPACE, "scratch %zu bytes, need %zu", scratch_bytes, need);
+    int32_t* kvl = (int32_t*)scratch;
+    uint8_t* kvalid = (uint8_t*)scratch + align_up((size_t)rows * 4, 16);
+    uint8_t* tfull = kvalid + (size_t)rows * Tp;
     AttnParams p;
-    p.qkv = qkv; p.o = o; p.rows = rows; p.T = T; p.H = H; p.hd = 64;
-    p.kv_len = kv_len; p.kv_mod = rows; p.key_mask = key_mask; p.mask_stride = T; p.P = 0;
+    p.qkv = qk; p.vt = vt; p.Tp = (int)Tp; p.o = o; p.rows = rows; p.T = T; p.H = H; p.hd = 64;
+    p.kv_len = kvl; p.kv_mod = rows; p.key_mask = key_mask; p.mask_stride = T; p.P = 0;
+    p.kvalid = kvalid; p.tile_full = tfull;
     (void)hipGetLastError();
+    launch_key_prep(key_mask, T, kv_len, rows, 0, T, (int)Tp, kvl, kvalid, tfull, (hipStream_t)stream);
     launch_attention_bf16(p, (hipStream_t)stream);
     hipError_t e = hipGetLastError();
     return e == hipSuccess ? CFM_OK : fail(CFM_E_HIP, "launch failed: %s", hipGetErrorString(e));

@@ -186,13 +186,21 @@ cfm_status cfm_gemm_bf16(const void* A, int a_is_f32, int lda, const void* W, in
                          const float* bias, int M, int N, int K, int epilogue,
                          const float* gate, void* C, int ldc, int tile, void* stream);
 
-/* Key-padding-masked multi-head attention, bf16 in / bf16 out, fp32 softmax.
- *   qkv device bf16 [rows, T, 3 * H * 64] (q | k | v, head j at columns j*64)
+/* Key-padding-masked multi-head attention, bf16 in / bf16 out, fp32 softmax
+ * (VoiceHub, "Attention" and the padding row of "Semantic-preserving and
+ * approximate changes": padded frames are fully masked):
+ *   o[row, q, head] = sum_k softmax_k(q.k / sqrt(64), masked keys excluded) v_k
+ *   qk device bf16 [rows, T, 2 * H * 64]: q at columns head*64, k at H*64 + head*64
+ *   vt device bf16 [rows, H, 64, Tp]: v transposed per head, Tp = T rounded up
+ *      to a multiple of 64 (entries past T are never used)
  *   kv_len device int32 [rows]: keys >= kv_len[row] are masked;
  *   key_mask device uint8 [rows, T] (1 = valid key) or NULL;
+ *   scratch device memory (16-byte aligned) of at least
+ *      rows * 4 + rows * Tp + rows * Tp / 64 + 64 bytes (key validity tables);
  *   o device bf16 [rows, T, H * 64]. A row with no valid key gives o = 0. */
-cfm_status cfm_attention_bf16(const void* qkv, const int32_t* kv_len, const uint8_t* key_mask,
-                              int rows, int T, int H, void* o, void* stream);
+cfm_status cfm_attention_bf16(const void* qk, const void* vt, const int32_t* kv_len,
+                              const uint8_t* key_mask, int rows, int T, int H, void* scratch,
+                              size_t scratch_bytes, void* o, void* stream);
 
 /* adaLN-modulated LayerNorm: y = LN(h) * (1 + scale) + shift, eps 1e-6, biased
  * variance, stats in fp32. h device fp32 [M, d]; shift, scale device fp32 [d];

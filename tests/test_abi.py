@@ -151,6 +151,8 @@ def test_single_kernel_entry_validation(lib):
     assert lib.cfm_gemm_bf16(1 << 20, 0, 16, 1 << 21, 16, None, 4, 4, 16, 3, None, 1 << 22, 4, 0, None) == 1
     assert lib.cfm_gemm_bf16(1 << 20, 0, 16, 1 << 21, 16, None, 4, 4, 16, 9, None, 1 << 22, 4, 0, None) == 4
     assert lib.cfm_gemm_bf16(1 << 20, 1, 16, 1 << 21, 16, None, 4, 4, 16, 0, None, 1 << 22, 4, 2, None) == 4
-    assert lib.cfm_attention_bf16(None, None, None, 2, 8, 1, None, None) == 1
-    assert lib.cfm_attention_bf16(None, None, None, 0, 8, 1, None, None) == 0
+    assert lib.cfm_attention_bf16(None, None, None, None, 2, 8, 1, None, 0, None, None) == 1
+    assert lib.cfm_attention_bf16(None, None, None, None, 0, 8, 1, None, 0, None, None) == 0
+    f = 1 << 20
+    assert lib.cfm_attention_bf16(f, f, f, None, 2, 8, 1, f, 10, f, None) == 6
     assert lib.cfm_adaln(1 << 20, 1 << 21, 1 << 22, 4, 30, 0, 1 << 23, None) == 2

@@ -133,6 +133,19 @@ def _attn_case(rows, T, H, seed, scale=1.0):
     return qkv
 
 
+def _attn_call(qkv, H, kv_len, o, mask=None):
+    """Split a [rows, T, 3d] q|k|v tensor into the kernel's q|k rows and per-head V^T."""
+    import flow_matching_tts_amd as F
+    rows, T, _ = qkv.shape
+    d = H * 64
+    Tp = (T + 63) // 64 * 64
+    vt = np.full((rows, H, 64, Tp), np.nan, np.float32)        # padding must never be read as valid
+    vt[..., :T] = qkv[..., 2 * d:].reshape(rows, T, H, 64).transpose(0, 2, 3, 1)
+    F.attention_bf16(dev(qkv[..., :2 * d], torch.bfloat16), dev(vt, torch.bfloat16), dev(kv_len), o,
+                     n_heads=H, key_mask=None if mask is None else dev(mask))
+    return o
+
+
 def _attn_ref(qkv, H, valid):
     rows, T, _ = qkv.shape
     d = H * 64
@@ -142,7 +155,7 @@ def _attn_ref(qkv, H, valid):
     return o.transpose(0, 2, 1, 3).reshape(rows, T, d)
 
 
-@pytest.mark.parametrize("rows,T,H", [(3, 200, 2), (2, 1, 1), (1, 128, 4), (2, 1000, 1), (4, 65, 3)])
+@pytest.mark.parametrize("rows,T,H", [(3, 200, 2), (2, 1, 1), (1, 128, 4), (2, 1000, 1), (4, 65, 3), (2, 513, 2)])
 def test_attention_bf16_matches_oracle(rows, T, H):
     import flow_matching_tts_amd as F
     qkv = _attn_case(rows, T, H, rows * T + H, scale=1.5)
@@ -153,7 +166,7 @@ def test_attention_bf16_matches_oracle(rows, T, H):
     mask[:, 0] = 1
     valid = (np.arange(T)[None] < kv_len[:, None]) & mask.astype(bool)
     o = torch.zeros((rows, T, H * 64), dtype=torch.bfloat16, device="cuda")
-    F.attention_bf16(dev(qkv, torch.bfloat16), dev(kv_len), o, n_heads=H, key_mask=dev(mask))
+    _attn_call(qkv, H, kv_len, o, mask)
     got = o.float().cpu().numpy()
     want = _attn_ref(qkv, H, valid)
     err = np.abs(got - want)
@@ -172,7 +185,7 @@ def test_attention_bf16_empty_and_single_key_rows():
     mask[2] = 0
     mask[2, 77] = 1
     o = torch.full((rows, T, H * 64), float("nan"), dtype=torch.bfloat16, device="cuda")
-    F.attention_bf16(dev(qkv, torch.bfloat16), dev(kv_len), o, n_heads=H, key_mask=dev(mask))
+    _attn_call(qkv, H, kv_len, o, mask)
     got = o.float().cpu().numpy()
     assert np.all(got[0] == 0.0)                      # no valid key -> 0
     d = H * 64
@@ -188,7 +201,7 @@ def test_attention_bf16_masked_keys_never_leak_non_finite_values():
     qkv[:, 100:, 64:] = np.inf          # k and v of padded keys
     kv_len = np.array([100, 100], np.int32)
     o = torch.zeros((rows, T, 64), dtype=torch.bfloat16, device="cuda")
-    F.attention_bf16(dev(qkv, torch.bfloat16), dev(kv_len), o, n_heads=H)
+    _attn_call(qkv, H, kv_len, o)
     got = o.float().cpu().numpy()
     assert np.all(np.isfinite(got[:, :100]))
     valid = np.arange(T)[None].repeat(rows, 0) < 100

@@ -49,7 +49,7 @@ def reduced(name):
     if name == "varlen_masked":
         return s.replace(n_layers=2, n_frames=400, n_requests=3, n_steps=3, varlen=(50, 400))
     if name == "multicond_rf":
-        return s.replace(n_layers=2, n_frames=200, n_requests=2, n_steps=3)
+        return s.replace(n_layers=2, n_frames=201, n_requests=2, n_steps=3)
     raise KeyError(name)
 
 
