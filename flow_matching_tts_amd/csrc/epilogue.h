@@ -69,4 +69,111 @@ __device__ __forceinline__ void epi_store4(const EpiParams& p, int m0, int M, in
         if (m0 + r < M) epi_store<EPI, ActT>(p, m0 + r, n, acc4[r]);
 }
 
+// Vector epilogue of 4 consecutive columns n..n+3 of one row m (in range, 16-byte
+// aligned). Same arithmetic as epi_store, one wide access per operand.
+template <int EPI>
+__device__ __forceinline__ void epi_store_vec4(const EpiParams& p, int m, int n, f32x4 v) {
+    if (p.bias) v += *(const f32x4*)(p.bias + n);
+    if constexpr (EPI == EPI_F32) {
+        *(f32x4*)((float*)p.out + (long long)m * p.ldo + n) = v;
+    } else if constexpr (EPI == EPI_ACT || EPI == EPI_GELU_ACT || EPI == EPI_QKV) {
+        if constexpr (EPI == EPI_GELU_ACT) {
+            v[0] = gelu_erf(v[0]); v[1] = gelu_erf(v[1]); v[2] = gelu_erf(v[2]); v[3] = gelu_erf(v[3]);
+        }
+        bf16x4 b;
+        b[0] = (bf16)v[0]; b[1] = (bf16)v[1]; b[2] = (bf16)v[2]; b[3] = (bf16)v[3];
+        *(bf16x4*)((bf16*)p.out + (long long)m * p.ldo + n) = b;
+    } else if constexpr (EPI == EPI_GATED) {
+        f32x4* h = (f32x4*)((float*)p.out + (long long)m * p.ldo + n);
+        *h += *(const f32x4*)(p.gate.at((long long)m) + n) * v;
+    } else if constexpr (EPI == EPI_INPROJ) {
+        const int r = m / p.Tx, t = m - r * p.Tx;
+        // v already holds acc + bias; the conditioned branches use acc + cproj instead
+        const f32x4 withc = p.cproj ? v - (p.bias ? *(const f32x4*)(p.bias + n) : f32x4{}) +
+                                          *(const f32x4*)(p.cproj + (long long)m * p.ldo + n)
+                                    : v;
+        for (int br = 0; br < p.nb; ++br) {
+            const long long tok = (long long)(br * p.R + r) * p.T + p.P + t;
+            *(f32x4*)((float*)p.out + tok * p.ldo + n) = br >= p.cond_branch0 ? withc : v;
+        }
+    } else if constexpr (EPI == EPI_VOUT) {
+        const int row = m / p.Tx, t = m - row * p.Tx;
+        const int r = row % p.R;
+        const bool valid = p.mask == nullptr || p.mask[(long long)r * p.Tx + t] != 0;
+        *(f32x4*)((float*)p.out + (long long)m * p.ldo + n) = valid ? v : f32x4{};
+    }
+}
+
+// Epilogue of one 32x32 MFMA accumulator block through a wave-private LDS
+// scratch area (32 rows x 36 floats, row-major): each lane writes its column
+// (16 scalar writes; a write instruction covers 32 consecutive columns of a
+// row), then reads back four consecutive columns of one row per access, so
+// every global access of the epilogue is 16 bytes wide (8 for bf16 outputs)
+// instead of one element. Value columns of the QKV projection are read back
+// down a column instead and written transposed (8 consecutive sequence
+// positions per store).
+constexpr int EPI_RP = 36;
+constexpr int EPI_WAVE_FLOATS = 32 * EPI_RP;
+
+template <int EPI>
+__device__ __forceinline__ void epi_block(const EpiParams& p, const f32x16& acc, float* wl, int mb, int nb0,
+                                          int M, int N, int lane) {
+    const int li = lane & 31, lh = lane >> 5;
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) wl[(8 * g + 4 * lh + r) * EPI_RP + li] = acc[g * 4 + r];
+    __builtin_amdgcn_wave_barrier();
+    if constexpr (EPI == EPI_QKV) {
+        if (nb0 >= p.d2) {
+            // lane: column li, rows 16 lh .. 16 lh + 15 (consecutive sequence positions)
+            const int n = nb0 + li;
+            if (n < N) {
+                const float b = p.bias ? p.bias[n] : 0.0f;
+                const int c = n - p.d2, hh = c >> 6, e = c & 63;
+#pragma unroll
+                for (int q8 = 0; q8 < 2; ++q8) {
+                    const int r0 = 16 * lh + 8 * q8, m = mb + r0;
+                    float vals[8];
+#pragma unroll
+                    for (int r = 0; r < 8; ++r) vals[r] = wl[(r0 + r) * EPI_RP + li] + b;
+                    const int row = m / p.T, t = m - row * p.T;
+                    if (m + 7 < M && t + 7 < p.T && (t & 7) == 0) {
+                        bf16x8 o;
+#pragma unroll
+                        for (int r = 0; r < 8; ++r) o[r] = (bf16)vals[r];
+                        *(bf16x8*)(p.vt + ((long long)(row * p.H + hh) * 64 + e) * p.Tp + t) = o;
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 8; ++r)
+                            if (m + r < M) {
+                                const int rw = (m + r) / p.T, tt = (m + r) - rw * p.T;
+                                p.vt[((long long)(rw * p.H + hh) * 64 + e) * p.Tp + tt] = (bf16)vals[r];
+                            }
+                    }
+                }
+            }
+            __builtin_amdgcn_wave_barrier();
+            return;
+        }
+    }
+    // lane: row (lane / 8) + 8 q, columns 4 (lane % 8) .. +3
+    const int c0 = (lane & 7) * 4;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int row = (lane >> 3) + 8 * q;
+        const f32x4 v = *(const f32x4*)(wl + row * EPI_RP + c0);
+        const int m = mb + row, n = nb0 + c0;
+        if (m >= M) continue;
+        if (n + 3 < N) {
+            epi_store_vec4<EPI>(p, m, n, v);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (n + e < N) epi_store<EPI, bf16>(p, m, n + e, v[e]);
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+}
+
 }  // namespace cfm

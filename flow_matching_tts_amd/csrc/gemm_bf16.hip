@@ -40,6 +40,7 @@ struct Cfg {
     static constexpr int CPR = BK / 8;                         // 16-byte chunks per row
     static constexpr int LDS_BYTES = 2 * (BM + BN) * LDK * 2;
     static_assert(TM >= 1 && TN >= 1 && WM % 32 == 0 && WN % 32 == 0, "wave tile");
+    static_assert(LDS_BYTES >= WGM * WGN * EPI_WAVE_FLOATS * 4, "epilogue staging fits in the operand LDS");
     static_assert((BM * CPR) % NT == 0 && (BN * CPR) % NT == 0, "chunk split");
 };
 
@@ -191,22 +192,15 @@ gemm_bf16_kernel(const AT* __restrict__ A, int lda, const bf16* __restrict__ W, 
         cur ^= 1;
     }
 
-    // accumulator layout of a 32x32 block: register g*4 + r holds
-    // row 8g + 4*(lane/32) + r, column lane%32.
+    // epilogue through LDS, reusing the operand buffers (every wave is past its
+    // last read of them once it passes this barrier)
+    __syncthreads();
+    float* wl = (float*)smem + wave * EPI_WAVE_FLOATS;
 #pragma unroll
     for (int i = 0; i < C::TM; ++i)
 #pragma unroll
-        for (int j = 0; j < C::TN; ++j) {
-            const int n = n0 + wn * C::WN + j * 32 + li;
-            if (n >= N) continue;
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int m = m0 + wm * C::WM + i * 32 + 8 * g + 4 * lh;
-                const float a4[4] = {acc[i][j][g * 4 + 0], acc[i][j][g * 4 + 1], acc[i][j][g * 4 + 2],
-                                     acc[i][j][g * 4 + 3]};
-                epi_store4<EPI, bf16>(ep, m, M, n, a4);
-            }
-        }
+        for (int j = 0; j < C::TN; ++j)
+            epi_block<EPI>(ep, acc[i][j], wl, m0 + wm * C::WM + i * 32, n0 + wn * C::WN + j * 32, M, N, lane);
 }
 
 template <typename C, typename AT, int EPI>
@@ -220,6 +214,160 @@ void launch_cfg(const AT* A, int lda, const bf16* W, int ldw, int M, int N, int 
     (void)attr;
     gemm_bf16_kernel<C, AT, EPI><<<tm * tn, C::NT, C::LDS_BYTES, s>>>(A, lda, W, ldw, M, N, K, tm, tn, ep);
 }
+
+// ---------------------------------------------------------------------------
+// Direct-to-LDS variant: operand tiles go from HBM straight into LDS
+// (buffer_load_dwordx4 ... lds: each lane's 16 bytes land at M0 + 16 * lane),
+// so no registers stage them and the pipeline runs deeper: a ring of 4 LDS
+// slots with K stage 32, the loads of stage k+3 issued while stage k is
+// multiplied. The loads are issued from inline assembly and their completion
+// is awaited explicitly (s_waitcnt vmcnt before the barrier that publishes a
+// stage), so the compiler neither knows about nor waits on them; the main loop
+// contains no other vector-memory instruction, and everything is drained before
+// the epilogue issues its own loads. M0 is written only by these sequences.
+// Rows are 64 bytes (unpadded); the four 16-byte chunks of a row are XOR-swizzled
+// by (row / 2) % 4 so that 8 consecutive rows read at the same k hit 8 distinct
+// bank groups.
+constexpr int DBK = 32;
+constexpr int NSLOT = 4;
+
+template <int BM_, int BN_, int WGM_, int WGN_>
+struct DCfg {
+    static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_;
+    static constexpr int NW = WGM * WGN, NT = 64 * NW;
+    static constexpr int WM = BM / WGM, WN = BN / WGN;
+    static constexpr int TM = WM / 32, TN = WN / 32;
+    static constexpr int A_INSTR = BM / 16 / NW, W_INSTR = BN / 16 / NW;   // 16 rows per wave instruction
+    static constexpr int L = A_INSTR + W_INSTR;                           // loads per wave per stage
+    static constexpr int SLOT = (BM + BN) * DBK;                          // bf16 elements per slot
+    static constexpr int LDS_BYTES = NSLOT * SLOT * 2;
+    static_assert(BM % (16 * NW) == 0 && BN % (16 * NW) == 0, "row groups");
+    static_assert(TM >= 1 && TN >= 1, "wave tile");
+    static_assert(LDS_BYTES >= NW * EPI_WAVE_FLOATS * 4, "epilogue staging fits in the ring");
+};
+
+__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 3); }
+
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, int voff, unsigned lds_addr) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :: "s"(lds_addr), "v"(voff), "s"(rs) : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory"); }
+
+__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
+
+template <int INSTR>
+__device__ __forceinline__ void dma_stage(__amdgpu_buffer_rsrc_t rs, int ld, int rows_total, int K, int r0,
+                                          int k0, unsigned slot_addr, int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < INSTR; ++i) {
+        const int grp = wave * INSTR + i;              // 16-row group, wave-uniform
+        const int row = grp * 16 + (lane >> 2);
+        const int c = swz(row, lane & 3);              // logical chunk this lane fetches
+        const int r = r0 + row, k = k0 + c * 8;
+        const int off = (r < rows_total && k < K) ? (r * ld + k) * 2 : OOB;
+        dma16(rs, off, __builtin_amdgcn_readfirstlane(slot_addr + grp * 16 * DBK * 2));
+    }
+}
+
+template <typename C>
+__device__ __forceinline__ void dma_compute(f32x16 (&acc)[C::TM][C::TN], const bf16* as, const bf16* ws,
+                                            int wm, int wn, int li, int lh) {
+#pragma unroll
+    for (int ks = 0; ks < DBK / 16; ++ks) {
+        bf16x8 a[C::TM], b[C::TN];
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i) {
+            const int row = wm * C::WM + i * 32 + li;
+            a[i] = *(const bf16x8*)(as + row * DBK + swz(row, ks * 2 + lh) * 8);
+        }
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j) {
+            const int row = wn * C::WN + j * 32 + li;
+            b[j] = *(const bf16x8*)(ws + row * DBK + swz(row, ks * 2 + lh) * 8);
+        }
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+            for (int j = 0; j < C::TN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+}
+
+template <typename C, int EPI>
+__global__ void __launch_bounds__(C::NT)
+gemm_dtl_kernel(const bf16* __restrict__ A, int lda, const bf16* __restrict__ W, int ldw,
+                int M, int N, int K, int tm, int tn, EpiParams ep) {
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    bf16* const ring = (bf16*)smem;           // NSLOT x [A: BM x DBK | W: BN x DBK]
+    const unsigned ring_addr = (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)smem;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int li = lane & 31, lh = lane >> 5;
+    const int wm = wave / C::WGN, wn = wave % C::WGN;
+    int mt, nt;
+    tile_of(blockIdx.x, tm * tn, tm, tn, mt, nt);
+    const int m0 = mt * C::BM, n0 = nt * C::BN;
+    const __amdgpu_buffer_rsrc_t ra = rsrc_of(A, (long long)M * lda * 2);
+    const __amdgpu_buffer_rsrc_t rw = rsrc_of(W, (long long)N * ldw * 2);
+    const int nk = (K + DBK - 1) / DBK;
+
+    f32x16 acc[C::TM][C::TN];
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j) acc[i][j] = f32x16{};
+
+    auto issue = [&](int stage) {
+        const unsigned slot = ring_addr + (unsigned)((stage % NSLOT) * C::SLOT * 2);
+        dma_stage<C::A_INSTR>(ra, lda, M, K, m0, stage * DBK, slot, wave, lane);
+        dma_stage<C::W_INSTR>(rw, ldw, N, K, n0, stage * DBK, slot + C::BM * DBK * 2, wave, lane);
+    };
+
+    for (int st = 0; st < NSLOT - 1 && st < nk; ++st) issue(st);
+    for (int kt = 0; kt < nk; ++kt) {
+        // this wave's loads of stage kt are done once at most the later issued
+        // stages (up to two) are still in flight; the barrier then publishes
+        // every wave's part and also frees slot (kt + 3) % 4, read at kt - 1
+        const int ahead = min(nk - 1, kt + NSLOT - 2) - kt;
+        if (ahead >= 2) wait_vm<2 * C::L>();
+        else if (ahead == 1) wait_vm<C::L>();
+        else wait_vm<0>();
+        barrier_only();
+        if (kt + NSLOT - 1 < nk) issue(kt + NSLOT - 1);
+        const bf16* slot = ring + (kt % NSLOT) * C::SLOT;
+        dma_compute<C>(acc, slot, slot + C::BM * DBK, wm, wn, li, lh);
+    }
+    wait_vm<0>();
+    // epilogue through LDS, reusing the operand buffers (every wave is past its
+    // last read of them once it passes this barrier)
+    __syncthreads();
+    float* wl = (float*)smem + wave * EPI_WAVE_FLOATS;
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j)
+            epi_block<EPI>(ep, acc[i][j], wl, m0 + wm * C::WM + i * 32, n0 + wn * C::WN + j * 32, M, N, lane);
+}
+
+template <typename C, int EPI>
+void launch_dcfg(const bf16* A, int lda, const bf16* W, int ldw, int M, int N, int K,
+                 const EpiParams& ep, hipStream_t s) {
+    const int tn = (N + C::BN - 1) / C::BN, tm = (M + C::BM - 1) / C::BM;
+    static const bool attr = [] {
+        return hipFuncSetAttribute((const void*)gemm_dtl_kernel<C, EPI>,
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES) == hipSuccess;
+    }();
+    (void)attr;
+    gemm_dtl_kernel<C, EPI><<<tm * tn, C::NT, C::LDS_BYTES, s>>>(A, lda, W, ldw, M, N, K, tm, tn, ep);
+}
+
+using D7 = DCfg<256, 256, 4, 2>;   // 8 waves, 64x128 per wave
+using D8 = DCfg<256, 256, 2, 2>;   // 4 waves, 128x128 per wave
+using D9 = DCfg<256, 256, 2, 4>;   // 8 waves, 128x64 per wave
 
 // tile configurations (index = the `tile` argument; 0 = automatic)
 using C1 = Cfg<128, 128, 32, 2, 2>;     // 4 waves, 64x64 per wave
@@ -239,7 +387,7 @@ void launch_epi(int tile, const AT* A, int lda, const bf16* W, int ldw, int M, i
         if (tile == 0) {
             // 256x256 tiles (8 waves) when they still give about one tile per CU or more
             const long long big = (long long)((M + 255) / 256) * ((N + 255) / 256);
-            tile = big >= 192 ? 5 : 6;
+            tile = big >= 192 ? 9 : 6;
         }
         switch (tile) {
             case 2: launch_cfg<C2, AT, EPI>(A, lda, W, ldw, M, N, K, ep, s); break;
@@ -247,6 +395,9 @@ void launch_epi(int tile, const AT* A, int lda, const bf16* W, int ldw, int M, i
             case 4: launch_cfg<C4, AT, EPI>(A, lda, W, ldw, M, N, K, ep, s); break;
             case 5: launch_cfg<C5, AT, EPI>(A, lda, W, ldw, M, N, K, ep, s); break;
             case 6: launch_cfg<C6, AT, EPI>(A, lda, W, ldw, M, N, K, ep, s); break;
+            case 7: launch_dcfg<D7, EPI>(A, lda, W, ldw, M, N, K, ep, s); break;
+            case 8: launch_dcfg<D8, EPI>(A, lda, W, ldw, M, N, K, ep, s); break;
+            case 9: launch_dcfg<D9, EPI>(A, lda, W, ldw, M, N, K, ep, s); break;
             default: launch_cfg<C1, AT, EPI>(A, lda, W, ldw, M, N, K, ep, s); break;
         }
     }
