@@ -225,52 +225,68 @@ attn_bf16_kernel(AttnParams p) {
 }
 
 constexpr int FQ = 64;          // queries per block on the fp32 path
-constexpr int FHD = 64;         // max head dim on the fp32 path
+constexpr int FKT = 64;         // keys per LDS tile on the fp32 path
 
+// fp32 path: one thread per query, exact fp32 online softmax; the block's keys
+// and values pass through LDS in tiles of 64 (HD = head dim, a multiple of 4).
+template <int HD_>
 __global__ void __launch_bounds__(FQ)
 attn_f32_kernel(AttnParams p) {
+    __shared__ float Kt[FKT][HD_ + 1];
+    __shared__ float Vs[FKT][HD_ + 1];
+    __shared__ float kb[FKT];
     const int row = blockIdx.z, head = blockIdx.y;
     const int q = blockIdx.x * FQ + threadIdx.x;
-    const int T = p.T, hd = p.hd, d = p.H * hd;
+    const int T = p.T, d = p.H * HD_;
     const long long ld = 3LL * d;
     const float* base = (const float*)p.qkv + (long long)row * T * ld;
     const int rr = row % p.kv_mod;
     const int kvl = min(p.kv_len[rr], T);
     const uint8_t* km = p.key_mask ? p.key_mask + (long long)rr * p.mask_stride : nullptr;
-    const float scale = 1.0f / sqrtf((float)hd);
+    const float scale = 1.0f / sqrtf((float)HD_);
     const int qc = q < T ? q : T - 1;
 
-    float qv[FHD], acc[FHD];
+    float qv[HD_], acc[HD_];
 #pragma unroll
-    for (int e = 0; e < FHD; ++e) {
-        qv[e] = e < hd ? base[(long long)qc * ld + head * hd + e] : 0.0f;
+    for (int e = 0; e < HD_; ++e) {
+        qv[e] = base[(long long)qc * ld + head * HD_ + e] * scale;
         acc[e] = 0.0f;
     }
     float m = -INFINITY, l = 0.0f;
-    for (int key = 0; key < kvl; ++key) {
-        if (!key_valid(p, km, key, kvl)) continue;
-        const float* kr = base + (long long)key * ld + d + head * hd;
-        float sdot = 0.0f;
+    for (int k0 = 0; k0 < kvl; k0 += FKT) {
+        __syncthreads();
+        for (int idx = threadIdx.x; idx < FKT * HD_; idx += FQ) {
+            const int kr = idx / HD_, e = idx % HD_;
+            const int key = k0 + kr;
+            const bool ok = key < kvl;
+            Kt[kr][e] = ok ? base[(long long)key * ld + d + head * HD_ + e] : 0.0f;
+            Vs[kr][e] = ok ? base[(long long)key * ld + 2 * d + head * HD_ + e] : 0.0f;
+        }
+        for (int kr = threadIdx.x; kr < FKT; kr += FQ) {
+            const int key = k0 + kr;
+            kb[kr] = key_valid(p, km, key, kvl) ? 1.0f : 0.0f;
+        }
+        __syncthreads();
+        const int nk = min(FKT, kvl - k0);
+        for (int kr = 0; kr < nk; ++kr) {
+            if (kb[kr] == 0.0f) continue;
+            float sdot = 0.0f;
 #pragma unroll
-        for (int e = 0; e < FHD; ++e)
-            if (e < hd) sdot = fmaf(qv[e], kr[e], sdot);
-        sdot *= scale;
-        const float m_new = fmaxf(m, sdot);
-        const float corr = expf(m - m_new);
-        const float pv = expf(sdot - m_new);
-        l = l * corr + pv;
-        const float* vr = kr + d;
+            for (int e = 0; e < HD_; ++e) sdot = fmaf(qv[e], Kt[kr][e], sdot);
+            const float m_new = fmaxf(m, sdot);
+            const float corr = expf(m - m_new);
+            const float pv = expf(sdot - m_new);
+            l = l * corr + pv;
 #pragma unroll
-        for (int e = 0; e < FHD; ++e)
-            if (e < hd) acc[e] = fmaf(pv, vr[e], acc[e] * corr);
-        m = m_new;
+            for (int e = 0; e < HD_; ++e) acc[e] = fmaf(pv, Vs[kr][e], acc[e] * corr);
+            m = m_new;
+        }
     }
     if (q < T) {
         const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-        float* dst = (float*)p.o + ((long long)row * T + q) * d + head * hd;
+        float* dst = (float*)p.o + ((long long)row * T + q) * d + head * HD_;
 #pragma unroll
-        for (int e = 0; e < FHD; ++e)
-            if (e < hd) dst[e] = acc[e] * inv;
+        for (int e = 0; e < HD_; ++e) dst[e] = acc[e] * inv;
     }
 }
 
@@ -282,10 +298,24 @@ void launch_attention_bf16(const AttnParams& p, hipStream_t s) {
     attn_bf16_kernel<<<grid, NT, 0, s>>>(p);
 }
 
+template <int HD_>
+void launch_f32_hd(const AttnParams& p, hipStream_t s) {
+    dim3 grid((p.T + FQ - 1) / FQ, p.H, p.rows);
+    attn_f32_kernel<HD_><<<grid, FQ, 0, s>>>(p);
+}
+
 void launch_attention_f32(const AttnParams& p, hipStream_t s) {
     if (p.rows <= 0 || p.T <= 0) return;
-    dim3 grid((p.T + FQ - 1) / FQ, p.H, p.rows);
-    attn_f32_kernel<<<grid, FQ, 0, s>>>(p);
+    switch (p.hd) {   // head dims the fp32 path supports: multiples of 4 up to 64
+        case 4: launch_f32_hd<4>(p, s); break;      case 8: launch_f32_hd<8>(p, s); break;
+        case 12: launch_f32_hd<12>(p, s); break;    case 16: launch_f32_hd<16>(p, s); break;
+        case 20: launch_f32_hd<20>(p, s); break;    case 24: launch_f32_hd<24>(p, s); break;
+        case 28: launch_f32_hd<28>(p, s); break;    case 32: launch_f32_hd<32>(p, s); break;
+        case 36: launch_f32_hd<36>(p, s); break;    case 40: launch_f32_hd<40>(p, s); break;
+        case 44: launch_f32_hd<44>(p, s); break;    case 48: launch_f32_hd<48>(p, s); break;
+        case 52: launch_f32_hd<52>(p, s); break;    case 56: launch_f32_hd<56>(p, s); break;
+        case 60: launch_f32_hd<60>(p, s); break;    default: launch_f32_hd<64>(p, s); break;
+    }
 }
 
 }  // namespace cfm

@@ -9,76 +9,130 @@ namespace {
 
 // ---------------------------------------------------------------------------
 // Fused CFG combine + Euler update (VoiceHub "Custom Triton and CUDA kernels":
-// packed CFG combination plus an Euler update in one pass). One float4 of x per
-// thread: x += sum_b (dt * w_b) * v_b, read once, written once; masked frames
-// are neither read nor written.
+// packed CFG combination plus an Euler update in one pass):
+// x += sum_b (dt * w_b) * v_b, read once, written once; masked frames are
+// neither read nor written. Each thread owns EU float4s of x spaced one grid
+// apart (coalesced per instruction) and issues all of their loads before any
+// arithmetic. One float4 per thread measured fastest (more per thread gives
+// fewer, longer-lived waves and no gain in bytes in flight).
+constexpr int EU = 1;
+
 __global__ void __launch_bounds__(256)
 cfg_euler_kernel(const f32x4* __restrict__ v, int nb, float w0, float w1, float w2,
                  const uint8_t* __restrict__ mask, long long n4, int c4, long long branch4,
                  f32x4* __restrict__ x) {
-    const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= n4) return;
-    if (mask != nullptr && mask[i / c4] == 0) return;
-    f32x4 acc = x[i];
-    acc += w0 * v[i];
-    if (nb > 1) acc += w1 * v[branch4 + i];
-    if (nb > 2) acc += w2 * v[2 * branch4 + i];
-    x[i] = acc;
+    const long long stride = (long long)gridDim.x * blockDim.x;
+    const long long i0 = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    f32x4 xv[EU], a[EU], b[EU], c[EU];
+    bool ok[EU];
+#pragma unroll
+    for (int u = 0; u < EU; ++u) {
+        const long long i = i0 + u * stride;
+        ok[u] = i < n4 && (mask == nullptr || mask[i / c4] != 0);
+        if (ok[u]) {
+            xv[u] = *(x + i);
+            a[u] = *(v + i);
+            if (nb > 1) b[u] = *(v + branch4 + i);
+            if (nb > 2) c[u] = *(v + 2 * branch4 + i);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < EU; ++u) {
+        if (!ok[u]) continue;
+        f32x4 acc = xv[u] + w0 * a[u];
+        if (nb > 1) acc += w1 * b[u];
+        if (nb > 2) acc += w2 * c[u];
+        x[i0 + u * stride] = acc;
+    }
 }
 
 // ---------------------------------------------------------------------------
-// adaLN LayerNorm, one wave per token: the row is held in registers, mean and
-// biased variance by two wave reductions (exact two-pass), then
-// y = (h - mean) * rsqrt(var + 1e-6) * (1 + scale) + shift.
-constexpr int LN_MAX4 = 16;   // d <= 4096
+// adaLN LayerNorm. A wave normalises TPW consecutive tokens; the row is held in
+// registers (V float4 per lane), mean and biased variance come from two wave
+// reductions (exact two-pass), then y = (h - mean) * rsqrt(var + 1e-6) *
+// (1 + scale) + shift. The shift/scale vectors are loaded once per wave and
+// reloaded only when a token belongs to another modulation group, and the next
+// token's row is loaded before the current one is reduced.
+constexpr int TPW = 4;
 
-template <bool OUT_BF16>
+template <bool OUT_BF16, int V>
 __global__ void __launch_bounds__(256)
 adaln_kernel(LnParams p) {
-    const long long o = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const long long o0 = ((long long)blockIdx.x * 4 + (threadIdx.x >> 6)) * TPW;
     const int lane = threadIdx.x & 63;
-    if (o >= p.n_out) return;
-    const long long row = o / p.Tout;
-    const int t = (int)(o - row * p.Tout);
-    const long long in_tok = row * p.Tin + p.off + t;
     const int d4 = p.d >> 2;
-    const f32x4* src = (const f32x4*)(p.h + in_tok * p.d);
-
-    f32x4 v[LN_MAX4];
-    float sum = 0.0f;
+    if (o0 >= p.n_out) return;
+    auto src_of = [&](long long o) {
+        const long long row = o / p.Tout;
+        const int t = (int)(o - row * p.Tout);
+        return (const f32x4*)(p.h + (row * p.Tin + p.off + t) * p.d);
+    };
+    f32x4 cur[V], nxt[V], sh[V], sc[V];
+    const float* sh_ptr = nullptr;
+    {
+        const f32x4* src = src_of(o0);
 #pragma unroll
-    for (int i = 0; i < LN_MAX4; ++i) {
-        const int c = lane + i * 64;
-        if (c < d4) {
-            v[i] = src[c];
-            sum += (v[i][0] + v[i][1]) + (v[i][2] + v[i][3]);
+        for (int i = 0; i < V; ++i) {
+            const int c = lane + i * 64;
+            cur[i] = c < d4 ? src[c] : f32x4{};
         }
     }
-    const float mean = wave_sum(sum) / (float)p.d;
-    float sq = 0.0f;
+#pragma unroll 1
+    for (int it = 0; it < TPW; ++it) {
+        const long long o = o0 + it;
+        if (o >= p.n_out) break;
+        const bool more = it + 1 < TPW && o + 1 < p.n_out;
+        if (more) {
+            const f32x4* src = src_of(o + 1);
 #pragma unroll
-    for (int i = 0; i < LN_MAX4; ++i) {
-        const int c = lane + i * 64;
-        if (c < d4) {
-            const f32x4 z = v[i] - mean;
-            sq += (z[0] * z[0] + z[1] * z[1]) + (z[2] * z[2] + z[3] * z[3]);
-        }
-    }
-    const float rstd = rsqrtf(wave_sum(sq) / (float)p.d + 1e-6f);
-    const f32x4* sh = (const f32x4*)p.shift.at(o);
-    const f32x4* sc = (const f32x4*)p.scale.at(o);
-#pragma unroll
-    for (int i = 0; i < LN_MAX4; ++i) {
-        const int c = lane + i * 64;
-        if (c < d4) {
-            const f32x4 y = (v[i] - mean) * rstd * (1.0f + sc[c]) + sh[c];
-            if constexpr (OUT_BF16) {
-                bf16x4 b;
-                b[0] = (bf16)y[0]; b[1] = (bf16)y[1]; b[2] = (bf16)y[2]; b[3] = (bf16)y[3];
-                ((bf16x4*)((bf16*)p.y + o * p.d))[c] = b;
-            } else {
-                ((f32x4*)((float*)p.y + o * p.d))[c] = y;
+            for (int i = 0; i < V; ++i) {
+                const int c = lane + i * 64;
+                nxt[i] = c < d4 ? src[c] : f32x4{};
             }
+        }
+        const float* shp = p.shift.at(o);
+        if (shp != sh_ptr) {              // wave-uniform
+            sh_ptr = shp;
+            const f32x4* s4 = (const f32x4*)shp;
+            const f32x4* c4 = (const f32x4*)p.scale.at(o);
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+                const int c = lane + i * 64;
+                sh[i] = c < d4 ? s4[c] : f32x4{};
+                sc[i] = c < d4 ? c4[c] + 1.0f : f32x4{};
+            }
+        }
+        float sum = 0.0f;
+#pragma unroll
+        for (int i = 0; i < V; ++i) sum += (cur[i][0] + cur[i][1]) + (cur[i][2] + cur[i][3]);
+        const float mean = wave_sum(sum) / (float)p.d;
+        float sq = 0.0f;
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+            const int c = lane + i * 64;
+            if (c < d4) {
+                const f32x4 z = cur[i] - mean;
+                sq += (z[0] * z[0] + z[1] * z[1]) + (z[2] * z[2] + z[3] * z[3]);
+            }
+        }
+        const float rstd = rsqrtf(wave_sum(sq) / (float)p.d + 1e-6f);
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+            const int c = lane + i * 64;
+            if (c < d4) {
+                const f32x4 y = (cur[i] - mean) * rstd * sc[i] + sh[i];
+                if constexpr (OUT_BF16) {
+                    bf16x4 b;
+                    b[0] = (bf16)y[0]; b[1] = (bf16)y[1]; b[2] = (bf16)y[2]; b[3] = (bf16)y[3];
+                    ((bf16x4*)((bf16*)p.y + o * p.d))[c] = b;
+                } else {
+                    ((f32x4*)((float*)p.y + o * p.d))[c] = y;
+                }
+            }
+        }
+        if (more) {
+#pragma unroll
+            for (int i = 0; i < V; ++i) cur[i] = nxt[i];
         }
     }
 }
@@ -159,16 +213,26 @@ void launch_cfg_euler(const float* v, int nb, float w0, float w1, float w2, cons
                       int R, int Tx, int C, float* x, hipStream_t s) {
     const long long n4 = (long long)R * Tx * C / 4;
     if (n4 <= 0) return;
-    const int blocks = (int)((n4 + 255) / 256);
+    const int blocks = (int)((n4 + 256LL * EU - 1) / (256LL * EU));
     cfg_euler_kernel<<<blocks, 256, 0, s>>>((const f32x4*)v, nb, w0, w1, w2, mask, n4, C / 4, n4,
                                              (f32x4*)x);
 }
 
+template <int V>
+void launch_adaln_v(const LnParams& p, hipStream_t s) {
+    const int blocks = (int)((p.n_out + 4 * TPW - 1) / (4 * TPW));
+    if (p.out_bf16) adaln_kernel<true, V><<<blocks, 256, 0, s>>>(p);
+    else adaln_kernel<false, V><<<blocks, 256, 0, s>>>(p);
+}
+
 void launch_adaln(const LnParams& p, hipStream_t s) {
     if (p.n_out <= 0) return;
-    const int blocks = (int)((p.n_out + 3) / 4);
-    if (p.out_bf16) adaln_kernel<true><<<blocks, 256, 0, s>>>(p);
-    else adaln_kernel<false><<<blocks, 256, 0, s>>>(p);
+    const int v = (p.d / 4 + 63) / 64;     // float4 per lane
+    if (v <= 1) launch_adaln_v<1>(p, s);
+    else if (v <= 2) launch_adaln_v<2>(p, s);
+    else if (v <= 4) launch_adaln_v<4>(p, s);
+    else if (v <= 8) launch_adaln_v<8>(p, s);
+    else launch_adaln_v<16>(p, s);
 }
 
 void launch_timestep_embedding(float* temb, int S, int F, hipStream_t s) {
