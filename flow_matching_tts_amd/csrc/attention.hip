@@ -36,9 +36,6 @@ namespace cfm {
 namespace {
 
 constexpr int HD = 64;
-constexpr int NW = 8;          // waves per block, 32 queries each
-constexpr int QT = 32 * NW;    // queries per block (they share every K / V^T tile)
-constexpr int NT = 64 * NW;
 constexpr int KT = 64;         // keys per LDS tile
 constexpr int KP = HD + 8;     // K tile row pitch (bf16): 144 B
 constexpr int VP = KT + 8;     // V^T tile row pitch (bf16): 144 B
@@ -57,9 +54,10 @@ __device__ __forceinline__ bool key_valid(const AttnParams& p, const uint8_t* km
 // One KV tile in registers on its way to LDS: KV_CH chunks of K (one key, 8
 // head dims each) and of V^T (one head dim, 8 keys each) per thread, with the
 // validity bytes of their keys. Masked keys are written as zeros.
-constexpr int KV_CH = KT * HD / 8 / NT;
-static_assert(KV_CH >= 1 && KT * HD / 8 % NT == 0, "tile split");
+template <int NT>
 struct KvStage {
+    static constexpr int KV_CH = KT * HD / 8 / NT;
+    static_assert(KV_CH >= 1 && KT * HD / 8 % NT == 0, "tile split");
     bf16x8 k[KV_CH], v[KV_CH];
     uint8_t kok[KV_CH];
     uint64_t vok[KV_CH];
@@ -93,8 +91,13 @@ struct KvStage {
     }
 };
 
-__global__ void __launch_bounds__(NT, 4)   // 4 waves per SIMD: two blocks per CU
+// NW waves per block, 32 queries each, all sharing every K / V^T tile: 8 for
+// long sequences; 1 for short ones (a block per 32 queries, no idle waves).
+template <int NW>
+__global__ void __launch_bounds__(64 * NW, 4)   // 4 waves per SIMD
 attn_bf16_kernel(AttnParams p) {
+    constexpr int QT = 32 * NW;    // queries per block
+    constexpr int NT = 64 * NW;
     __shared__ __attribute__((aligned(16))) bf16 Ks[2][KT * KP];
     __shared__ __attribute__((aligned(16))) bf16 Vt[2][HD * VP];
     __shared__ float kbias[2][KT];
@@ -131,7 +134,7 @@ attn_bf16_kernel(AttnParams p) {
         const int cur = it & 1;
         const bool full = tfull[it] != 0;
         {
-            KvStage st;
+            KvStage<NT> st;
             st.load(kbase, ldk, T - 1, vtbase, p.Tp, kv, it * KT, tid);
             st.store(Ks[cur], Vt[cur], kbias[cur], tid);
         }
@@ -294,8 +297,13 @@ attn_f32_kernel(AttnParams p) {
 
 void launch_attention_bf16(const AttnParams& p, hipStream_t s) {
     if (p.rows <= 0 || p.T <= 0) return;
-    dim3 grid((p.T + QT - 1) / QT, p.H, p.rows);
-    attn_bf16_kernel<<<grid, NT, 0, s>>>(p);
+    if (p.T <= 64) {
+        dim3 grid((p.T + 31) / 32, p.H, p.rows);
+        attn_bf16_kernel<1><<<grid, 64, 0, s>>>(p);
+    } else {
+        dim3 grid((p.T + 255) / 256, p.H, p.rows);
+        attn_bf16_kernel<8><<<grid, 512, 0, s>>>(p);
+    }
 }
 
 template <int HD_>

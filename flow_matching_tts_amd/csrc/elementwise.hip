@@ -1,6 +1,7 @@
 // Bandwidth-bound kernels: fused CFG combine + Euler update, adaLN-modulated
 // LayerNorm, and the small set-up kernels of a sampling call (timestep
 // embedding, per-request key lengths, conditioning vectors, prefix tokens).
+#include <algorithm>
 #include <math.h>
 #include "kernels.h"
 
@@ -47,7 +48,7 @@ cfg_euler_kernel(const f32x4* __restrict__ v, int nb, float w0, float w1, float 
 }
 
 // ---------------------------------------------------------------------------
-// adaLN LayerNorm. A wave normalises TPW consecutive tokens; the row is held in
+// adaLN LayerNorm. A wave normalises tpw (1..TPW) consecutive tokens; the row is held in
 // registers (V float4 per lane), mean and biased variance come from two wave
 // reductions (exact two-pass), then y = (h - mean) * rsqrt(var + 1e-6) *
 // (1 + scale) + shift. The shift/scale vectors are loaded once per wave and
@@ -57,8 +58,8 @@ constexpr int TPW = 4;
 
 template <bool OUT_BF16, int V>
 __global__ void __launch_bounds__(256)
-adaln_kernel(LnParams p) {
-    const long long o0 = ((long long)blockIdx.x * 4 + (threadIdx.x >> 6)) * TPW;
+adaln_kernel(LnParams p, int tpw) {
+    const long long o0 = ((long long)blockIdx.x * 4 + (threadIdx.x >> 6)) * tpw;
     const int lane = threadIdx.x & 63;
     const int d4 = p.d >> 2;
     if (o0 >= p.n_out) return;
@@ -78,10 +79,10 @@ adaln_kernel(LnParams p) {
         }
     }
 #pragma unroll 1
-    for (int it = 0; it < TPW; ++it) {
+    for (int it = 0; it < tpw; ++it) {
         const long long o = o0 + it;
         if (o >= p.n_out) break;
-        const bool more = it + 1 < TPW && o + 1 < p.n_out;
+        const bool more = it + 1 < tpw && o + 1 < p.n_out;
         if (more) {
             const f32x4* src = src_of(o + 1);
 #pragma unroll
@@ -220,9 +221,11 @@ void launch_cfg_euler(const float* v, int nb, float w0, float w1, float w2, cons
 
 template <int V>
 void launch_adaln_v(const LnParams& p, hipStream_t s) {
-    const int blocks = (int)((p.n_out + 4 * TPW - 1) / (4 * TPW));
-    if (p.out_bf16) adaln_kernel<true, V><<<blocks, 256, 0, s>>>(p);
-    else adaln_kernel<false, V><<<blocks, 256, 0, s>>>(p);
+    // several tokens per wave only when there are enough waves to fill the chip
+    const int tpw = (int)std::max<long long>(1, std::min<long long>(TPW, p.n_out / 2048));
+    const int blocks = (int)((p.n_out + 4 * tpw - 1) / (4 * tpw));
+    if (p.out_bf16) adaln_kernel<true, V><<<blocks, 256, 0, s>>>(p, tpw);
+    else adaln_kernel<false, V><<<blocks, 256, 0, s>>>(p, tpw);
 }
 
 void launch_adaln(const LnParams& p, hipStream_t s) {

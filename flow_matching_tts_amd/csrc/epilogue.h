@@ -105,14 +105,14 @@ __device__ __forceinline__ void epi_store_vec4(const EpiParams& p, int m, int n,
 }
 
 // Epilogue of one 32x32 MFMA accumulator block through a wave-private LDS
-// scratch area (32 rows x 36 floats, row-major): each lane writes its column
+// scratch area (32 rows x 32 floats, row-major, 4 KiB): each lane writes its column
 // (16 scalar writes; a write instruction covers 32 consecutive columns of a
 // row), then reads back four consecutive columns of one row per access, so
 // every global access of the epilogue is 16 bytes wide (8 for bf16 outputs)
 // instead of one element. Value columns of the QKV projection are read back
 // down a column instead and written transposed (8 consecutive sequence
 // positions per store).
-constexpr int EPI_RP = 36;
+constexpr int EPI_RP = 32;
 constexpr int EPI_WAVE_FLOATS = 32 * EPI_RP;
 
 template <int EPI>

@@ -20,6 +20,7 @@
 //
 // fp32 A operands (latent x and condition features) are rounded to bf16 while
 // being staged, so no separate conversion pass touches HBM.
+#include <algorithm>
 #include <type_traits>
 
 #include "epilogue.h"
@@ -376,6 +377,7 @@ using C3 = Cfg<256, 256, 32, 2, 4>;     // 8 waves, 128x64 per wave
 using C4 = Cfg<256, 128, 64, 2, 2>;     // 4 waves, 128x64 per wave
 using C5 = Cfg<256, 256, 64, 4, 2>;     // 8 waves, 64x128 per wave
 using C6 = Cfg<128, 128, 64, 2, 2>;     // 4 waves, 64x64 per wave, deeper K stage
+using C10 = Cfg<64, 64, 64, 2, 2>;      // 4 waves, 32x32 per wave: small problems
 using CF = Cfg<128, 128, 32, 2, 2>;     // fp32 A operands
 
 template <typename AT, int EPI>
@@ -385,9 +387,10 @@ void launch_epi(int tile, const AT* A, int lda, const bf16* W, int ldw, int M, i
         launch_cfg<CF, AT, EPI>(A, lda, W, ldw, M, N, K, ep, s);
     } else {
         if (tile == 0) {
-            // 256x256 tiles (8 waves) when they still give about one tile per CU or more
+            // the largest tile that still gives about one tile per CU or more
             const long long big = (long long)((M + 255) / 256) * ((N + 255) / 256);
-            tile = big >= 192 ? 9 : 6;
+            const long long mid = (long long)((M + 127) / 128) * ((N + 127) / 128);
+            tile = big >= 192 ? 9 : mid >= 160 ? 6 : 10;
         }
         switch (tile) {
             case 2: launch_cfg<C2, AT, EPI>(A, lda, W, ldw, M, N, K, ep, s); break;
@@ -398,6 +401,7 @@ void launch_epi(int tile, const AT* A, int lda, const bf16* W, int ldw, int M, i
             case 7: launch_dcfg<D7, EPI>(A, lda, W, ldw, M, N, K, ep, s); break;
             case 8: launch_dcfg<D8, EPI>(A, lda, W, ldw, M, N, K, ep, s); break;
             case 9: launch_dcfg<D9, EPI>(A, lda, W, ldw, M, N, K, ep, s); break;
+            case 10: launch_cfg<C10, AT, EPI>(A, lda, W, ldw, M, N, K, ep, s); break;
             default: launch_cfg<C1, AT, EPI>(A, lda, W, ldw, M, N, K, ep, s); break;
         }
     }

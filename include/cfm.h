@@ -180,8 +180,10 @@ cfm_status cfm_cfg_euler(const float* v, const float* w, int nb, float dt, const
  *   3: gated residual C(fp32) += gate[n] * (acc + bias[n]) with gate device fp32 [N].
  * K % 8 == 0 (bf16 A) or K % 4 == 0 (fp32 A); lda, ldw multiples of 8 (bf16)
  * or 4 (fp32 A); ldw >= K rounded up to 8 with zero padding.
- * tile: 0 = chosen from the problem size (what cfm_sample uses), 1 = 128x128
- * output tiles, 2 = 256x256 output tiles (bf16 A only). */
+ * tile: 0 = chosen from the problem size (what cfm_sample uses); 1..10 force
+ * one tile configuration (1 = 128x128, 2..5 = 256x256 / 256x128 register-staged,
+ * 6 = 128x128 with K stage 64, 7..9 = 256x256 direct-to-LDS, 10 = 64x64);
+ * configurations above 1 need a bf16 A operand. */
 cfm_status cfm_gemm_bf16(const void* A, int a_is_f32, int lda, const void* W, int ldw,
                          const float* bias, int M, int N, int K, int epilogue,
                          const float* gate, void* C, int ldc, int tile, void* stream);

@@ -86,7 +86,7 @@ def _gemm_ref(A, W, bias, epi, gate=None, c0=None):
 @pytest.mark.parametrize("M,N,K", [(300, 200, 136), (128, 128, 64), (1, 3, 8), (1000, 100, 1024), (257, 3072, 1024),
                                    (520, 600, 2048)])
 @pytest.mark.parametrize("epi", [0, 1, 2, 3])
-@pytest.mark.parametrize("tile", [1, 2, 3, 4, 5, 6, 7, 8, 9])
+@pytest.mark.parametrize("tile", [1, 2, 3, 4, 5, 6, 7, 8, 9, 10])
 def test_gemm_bf16_epilogues(M, N, K, epi, tile):
     import flow_matching_tts_amd as F
     rng = np.random.default_rng(M * 7 + N + K + epi)
@@ -155,7 +155,7 @@ def _attn_ref(qkv, H, valid):
     return o.transpose(0, 2, 1, 3).reshape(rows, T, d)
 
 
-@pytest.mark.parametrize("rows,T,H", [(3, 200, 2), (2, 1, 1), (1, 128, 4), (2, 1000, 1), (4, 65, 3), (2, 513, 2)])
+@pytest.mark.parametrize("rows,T,H", [(3, 200, 2), (2, 1, 1), (1, 128, 4), (2, 1000, 1), (4, 65, 3), (2, 513, 2), (3, 40, 2), (2, 64, 1)])
 def test_attention_bf16_matches_oracle(rows, T, H):
     import flow_matching_tts_amd as F
     qkv = _attn_case(rows, T, H, rows * T + H, scale=1.5)
