@@ -105,9 +105,21 @@ attn_bf16_kernel(AttnParams p) {
     const int row = blockIdx.z, head = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int j = lane & 31, h = lane >> 5;
-    const int T = p.T, d = p.H * HD;
+    // first token of the row and its length: padded rows hold T tokens each,
+    // packed rows row_off[row + 1] - row_off[row]
+    long long rbase;
+    int T;
+    if (p.row_off) {
+        rbase = p.row_off[row];
+        T = p.row_off[row + 1] - (int)rbase;
+        if (blockIdx.x * QT >= T) return;     // block-uniform: no query of this block exists
+    } else {
+        rbase = (long long)row * p.T;
+        T = p.T;
+    }
+    const int d = p.H * HD;
     const long long ldk = 2LL * d;
-    const bf16* qbase = (const bf16*)p.qkv + (long long)row * T * ldk + head * HD;
+    const bf16* qbase = (const bf16*)p.qkv + rbase * ldk + head * HD;
     const bf16* kbase = qbase + d;
     const bf16* vtbase = (const bf16*)p.vt + (long long)(row * p.H + head) * HD * p.Tp;
     const int q = blockIdx.x * QT + wave * 32 + j;
@@ -214,7 +226,7 @@ attn_bf16_kernel(AttnParams p) {
     const float l = l_part + __shfl_xor(l_part, 32, 64);
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
     if (q < T) {
-        bf16* dst = (bf16*)p.o + ((long long)row * T + q) * d + head * HD;
+        bf16* dst = (bf16*)p.o + (rbase + q) * d + head * HD;
 #pragma unroll
         for (int dt = 0; dt < 2; ++dt)
 #pragma unroll

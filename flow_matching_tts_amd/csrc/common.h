@@ -34,19 +34,21 @@ __device__ __forceinline__ float gelu_erf(float x) {
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
 
 // Where a row's modulation vectors live. Rows are branch-major (row = b*R + r);
-// token m belongs to row m / tokens_per_row. Every row reads conditioning
+// token m belongs to row m / tokens_per_row, or to row tok_row[m] in the packed
+// layout of a variable-length batch. Every row reads conditioning
 // vector 0 except the rows of branch `spk_branch`, whose condition carries the
 // request's speaker vector and reads vector 1 + r.
 struct RowMod {
-    const float* base;      // vector 0 of the current step, already offset to the chunk
-    long long cvec_stride;  // floats between consecutive conditioning vectors
-    int tokens_per_row;
-    int n_requests;
-    int spk_branch;         // -1: every row uses vector 0
+    const float* base = nullptr;       // vector 0 of the current step, already offset to the chunk
+    long long cvec_stride = 0;         // floats between consecutive conditioning vectors
+    int tokens_per_row = 1;
+    int n_requests = 1;
+    int spk_branch = -1;               // -1: every row uses vector 0
+    const int32_t* tok_row = nullptr;  // packed rows: row of each token (else m / tokens_per_row)
 
     __device__ __forceinline__ const float* at(long long m) const {
         if (spk_branch < 0) return base;
-        int row = (int)(m / tokens_per_row);
+        int row = tok_row ? tok_row[m] : (int)(m / tokens_per_row);
         int b = row / n_requests;
         int r = row - b * n_requests;
         return base + (b == spk_branch ? (long long)(1 + r) * cvec_stride : 0);

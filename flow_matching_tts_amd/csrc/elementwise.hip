@@ -62,6 +62,7 @@ adaln_kernel(LnParams p, int tpw) {
     const long long o0 = ((long long)blockIdx.x * 4 + (threadIdx.x >> 6)) * tpw;
     const int lane = threadIdx.x & 63;
     const int d4 = p.d >> 2;
+    if (p.n_dev) p.n_out = min(p.n_out, (long long)*p.n_dev);
     if (o0 >= p.n_out) return;
     auto src_of = [&](long long o) {
         const long long row = o / p.Tout;
@@ -187,6 +188,48 @@ __global__ void key_prep_kernel(const uint8_t* mask, int mask_stride, const int3
     if (threadIdx.x == 0) kv_len_out[r] = kvl;
 }
 
+// Row offsets of the packed layout: one block, each thread sums a contiguous
+// run of rows, the run totals are scanned in LDS (Hillis-Steele), and the runs
+// are written out. Row i = b*R + r holds kv_len[r] tokens rounded up to a
+// multiple of 8, so that every row starts 8-token aligned.
+constexpr int PACK_NT = 256;
+__global__ void __launch_bounds__(PACK_NT) pack_offsets_kernel(const int32_t* kv_len, int R, int N, int32_t* row_off) {
+    __shared__ int part[PACK_NT];
+    const int tid = threadIdx.x;
+    const int per = (N + PACK_NT - 1) / PACK_NT;
+    const int lo = min(N, tid * per), hi = min(N, lo + per);
+    int sum = 0;
+    for (int i = lo; i < hi; ++i) sum += (kv_len[i % R] + 7) & ~7;
+    part[tid] = sum;
+    __syncthreads();
+    for (int o = 1; o < PACK_NT; o <<= 1) {
+        const int v = tid >= o ? part[tid - o] : 0;
+        __syncthreads();
+        part[tid] += v;
+        __syncthreads();
+    }
+    int run = part[tid] - sum;   // exclusive prefix of this thread's run
+    for (int i = lo; i < hi; ++i) {
+        row_off[i] = run;
+        run += (kv_len[i % R] + 7) & ~7;
+    }
+    if (tid == PACK_NT - 1) row_off[N] = part[tid];
+}
+
+// tok_row[t] = the row holding packed token t (the last row whose offset is
+// <= t, which skips empty rows), -1 from row_off[N] on.
+__global__ void pack_rows_kernel(const int32_t* row_off, int N, int NTmax, int32_t* tok_row) {
+    const int t = blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= NTmax) return;
+    if (t >= row_off[N]) { tok_row[t] = -1; return; }
+    int lo = 0, hi = N - 1;   // row_off[lo] <= t < row_off[hi + 1]
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (row_off[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    tok_row[t] = lo;
+}
+
 __global__ void assemble_cvec_kernel(const float* ct, const float* bs, const float* spkproj,
                                      int nc, int d, float* cvec) {
     const int n = blockIdx.x * blockDim.x + threadIdx.x;
@@ -248,6 +291,14 @@ void launch_key_prep(const uint8_t* mask, int mask_stride, const int32_t* kv_len
                      hipStream_t s) {
     if (R <= 0) return;
     key_prep_kernel<<<R, 256, 0, s>>>(mask, mask_stride, kv_len_in, P, T, Tp, kv_len_out, kvalid, tile_full);
+}
+
+void launch_pack_rows(const int32_t* kv_len, int R, int nb, int NTmax, int32_t* row_off, int32_t* tok_row,
+                      hipStream_t s) {
+    const int N = nb * R;
+    if (N <= 0) return;
+    pack_offsets_kernel<<<1, PACK_NT, 0, s>>>(kv_len, R, N, row_off);
+    if (NTmax > 0) pack_rows_kernel<<<(NTmax + 255) / 256, 256, 0, s>>>(row_off, N, NTmax, tok_row);
 }
 
 void launch_assemble_cvec(const float* ct, const float* bs, const float* spkproj, int S, int nc,

@@ -26,47 +26,33 @@ __device__ __forceinline__ void epi_store(const EpiParams& p, int m, int n, floa
         const float plain = acc + b;
         const float withc = p.cproj ? acc + p.cproj[(long long)m * p.ldo + n] : plain;
         for (int br = 0; br < p.nb; ++br) {
-            long long tok = (long long)(br * p.R + r) * p.T + p.P + t;
+            long long tok;
+            if (p.row_off) {
+                const int row = br * p.R + r;
+                if (t >= p.row_off[row + 1] - p.row_off[row]) continue;   // past the row's last valid frame
+                tok = p.row_off[row] + t;
+            } else {
+                tok = (long long)(br * p.R + r) * p.T + p.P + t;
+            }
             ((float*)p.out)[tok * p.ldo + n] = br >= p.cond_branch0 ? withc : plain;
         }
     } else if constexpr (EPI == EPI_QKV) {
         if (n < p.d2) {
             ((bf16*)p.out)[(long long)m * p.ldo + n] = (bf16)(acc + b);
         } else {
-            const int row = m / p.T, t = m - row * p.T;
+            const int row = p.tok_row ? p.tok_row[m] : m / p.T;
+            const int t = m - (p.tok_row ? p.row_off[row] : row * p.T);
             const int c = n - p.d2, hh = c >> 6, e = c & 63;
             p.vt[((long long)(row * p.H + hh) * 64 + e) * p.Tp + t] = (bf16)(acc + b);
         }
     } else if constexpr (EPI == EPI_VOUT) {
-        const int row = m / p.Tx, t = m - row * p.Tx;
+        const int row = p.tok_row ? p.tok_row[m] : m / p.Tx;
+        const int t = m - (p.tok_row ? p.row_off[row] : row * p.Tx);
+        if (t >= p.Tx) return;   // packed rows: alignment tokens past the last frame
         const int r = row % p.R;
         const bool valid = p.mask == nullptr || p.mask[(long long)r * p.Tx + t] != 0;
-        ((float*)p.out)[(long long)m * p.ldo + n] = valid ? acc + b : 0.0f;
+        ((float*)p.out)[((long long)row * p.Tx + t) * p.ldo + n] = valid ? acc + b : 0.0f;
     }
-}
-
-// Four consecutive rows m0..m0+3 of one column (one lane's registers g*4 + 0..3).
-// EPI_QKV stores the four transposed values of a value column as one 8-byte
-// write when they belong to the same sequence row; everything else goes per element.
-template <int EPI, typename ActT>
-__device__ __forceinline__ void epi_store4(const EpiParams& p, int m0, int M, int n, const float* acc4) {
-    if constexpr (EPI == EPI_QKV) {
-        if (n >= p.d2 && m0 + 3 < M) {
-            const int row = m0 / p.T, t = m0 - row * p.T;
-            if (t + 3 < p.T && (t & 3) == 0) {
-                const float b = p.bias ? p.bias[n] : 0.0f;
-                const int c = n - p.d2, hh = c >> 6, e = c & 63;
-                bf16x4 v;
-                v[0] = (bf16)(acc4[0] + b); v[1] = (bf16)(acc4[1] + b);
-                v[2] = (bf16)(acc4[2] + b); v[3] = (bf16)(acc4[3] + b);
-                *(bf16x4*)(p.vt + ((long long)(row * p.H + hh) * 64 + e) * p.Tp + t) = v;
-                return;
-            }
-        }
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-        if (m0 + r < M) epi_store<EPI, ActT>(p, m0 + r, n, acc4[r]);
 }
 
 // Vector epilogue of 4 consecutive columns n..n+3 of one row m (in range, 16-byte
@@ -93,14 +79,23 @@ __device__ __forceinline__ void epi_store_vec4(const EpiParams& p, int m, int n,
                                           *(const f32x4*)(p.cproj + (long long)m * p.ldo + n)
                                     : v;
         for (int br = 0; br < p.nb; ++br) {
-            const long long tok = (long long)(br * p.R + r) * p.T + p.P + t;
+            long long tok;
+            if (p.row_off) {
+                const int row = br * p.R + r;
+                if (t >= p.row_off[row + 1] - p.row_off[row]) continue;   // past the row's last valid frame
+                tok = p.row_off[row] + t;
+            } else {
+                tok = (long long)(br * p.R + r) * p.T + p.P + t;
+            }
             *(f32x4*)((float*)p.out + tok * p.ldo + n) = br >= p.cond_branch0 ? withc : v;
         }
     } else if constexpr (EPI == EPI_VOUT) {
-        const int row = m / p.Tx, t = m - row * p.Tx;
+        const int row = p.tok_row ? p.tok_row[m] : m / p.Tx;
+        const int t = m - (p.tok_row ? p.row_off[row] : row * p.Tx);
+        if (t >= p.Tx) return;   // packed rows: alignment tokens past the last frame
         const int r = row % p.R;
         const bool valid = p.mask == nullptr || p.mask[(long long)r * p.Tx + t] != 0;
-        *(f32x4*)((float*)p.out + (long long)m * p.ldo + n) = valid ? v : f32x4{};
+        *(f32x4*)((float*)p.out + ((long long)row * p.Tx + t) * p.ldo + n) = valid ? v : f32x4{};
     }
 }
 
@@ -137,12 +132,22 @@ __device__ __forceinline__ void epi_block(const EpiParams& p, const f32x16& acc,
                     float vals[8];
 #pragma unroll
                     for (int r = 0; r < 8; ++r) vals[r] = wl[(r0 + r) * EPI_RP + li] + b;
-                    const int row = m / p.T, t = m - row * p.T;
-                    if (m + 7 < M && t + 7 < p.T && (t & 7) == 0) {
+                    if (m >= M) continue;
+                    const int row = p.tok_row ? p.tok_row[m] : m / p.T;
+                    const int t = m - (p.tok_row ? p.row_off[row] : row * p.T);
+                    const int len = p.tok_row ? p.row_off[row + 1] - p.row_off[row] : p.T;
+                    if (m + 7 < M && t + 7 < len && (t & 7) == 0) {
                         bf16x8 o;
 #pragma unroll
                         for (int r = 0; r < 8; ++r) o[r] = (bf16)vals[r];
                         *(bf16x8*)(p.vt + ((long long)(row * p.H + hh) * 64 + e) * p.Tp + t) = o;
+                    } else if (p.tok_row) {   // rare (row boundaries): rolled, reads LDS again
+#pragma unroll 1
+                        for (int r = 0; r < 8 && m + r < M; ++r) {
+                            const int rw = p.tok_row[m + r], tt = (m + r) - p.row_off[rw];
+                            p.vt[((long long)(rw * p.H + hh) * 64 + e) * p.Tp + tt] =
+                                (bf16)(wl[(r0 + r) * EPI_RP + li] + b);
+                        }
                     } else {
 #pragma unroll
                         for (int r = 0; r < 8; ++r)

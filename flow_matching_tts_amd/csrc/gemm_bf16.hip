@@ -137,6 +137,10 @@ gemm_bf16_kernel(const AT* __restrict__ A, int lda, const bf16* __restrict__ W, 
     int mt, nt;
     tile_of(blockIdx.x, tm * tn, tm, tn, mt, nt);
     const int m0 = mt * C::BM, n0 = nt * C::BN;
+    if (ep.m_dev) {
+        M = min(M, *ep.m_dev);
+        if (m0 >= M) return;
+    }
 
     f32x16 acc[C::TM][C::TN];
 #pragma unroll
@@ -312,6 +316,10 @@ gemm_dtl_kernel(const bf16* __restrict__ A, int lda, const bf16* __restrict__ W,
     int mt, nt;
     tile_of(blockIdx.x, tm * tn, tm, tn, mt, nt);
     const int m0 = mt * C::BM, n0 = nt * C::BN;
+    if (ep.m_dev) {
+        M = min(M, *ep.m_dev);
+        if (m0 >= M) return;
+    }
     const __amdgpu_buffer_rsrc_t ra = rsrc_of(A, (long long)M * lda * 2);
     const __amdgpu_buffer_rsrc_t rw = rsrc_of(W, (long long)N * ldw * 2);
     const int nk = (K + DBK - 1) / DBK;

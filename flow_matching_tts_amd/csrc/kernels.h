@@ -33,6 +33,16 @@ struct EpiParams {
     // vt[((row*H + hh)*64 + (n-2d)%64)*Tp + t]; q and k columns go to out with row stride ldo (= 2d)
     bf16* vt = nullptr;
     int H = 0, Tp = 0, d2 = 0;
+    // packed rows (variable-length batches): token m of the packed layout
+    // belongs to row tok_row[m] at position m - row_off[row]; row i holds
+    // row_off[i + 1] - row_off[i] tokens (its frame count rounded up to a
+    // multiple of 8; positions past Tx are never stored). Null: rows padded to
+    // T (or Tx) tokens.
+    const int32_t* tok_row = nullptr;
+    const int32_t* row_off = nullptr;
+    // optional device row count (at most M): the grid is sized for M and the
+    // tiles past *m_dev exit at once
+    const int32_t* m_dev = nullptr;
 };
 
 // bf16 MFMA GEMM, A bf16 or f32 (rounded to bf16 while staging), W bf16 [N, K].
@@ -58,6 +68,9 @@ struct AttnParams {
     // "all valid" bytes [(row % kv_mod), Tp / 64], made by launch_key_prep
     const uint8_t* kvalid;
     const uint8_t* tile_full;
+    // packed rows: row i's q|k rows start at token row_off[i] (else i * T); the
+    // row's query count is then its key length
+    const int32_t* row_off = nullptr;
 };
 void launch_attention_bf16(const AttnParams& p, hipStream_t s);
 void launch_attention_f32(const AttnParams& p, hipStream_t s);
@@ -71,6 +84,7 @@ struct LnParams {
     int Tin, Tout, off;
     RowMod shift, scale;      // RowMod evaluated on the OUTPUT token index
     int out_bf16;
+    const int32_t* n_dev = nullptr;   // optional device count of output tokens (at most n_out)
 };
 void launch_adaln(const LnParams& p, hipStream_t s);
 
@@ -86,6 +100,12 @@ void launch_timestep_embedding(float* temb, int S, int F, hipStream_t s);
 void launch_key_prep(const uint8_t* mask, int mask_stride, const int32_t* kv_len_in, int R, int P,
                      int T, int Tp, int32_t* kv_len_out, uint8_t* kvalid, uint8_t* tile_full,
                      hipStream_t s);
+// Packed row layout of a variable-length batch: rows are branch-major (row =
+// b*R + r) and row i holds kv_len[r] tokens rounded up to a multiple of 8;
+// row_off[N + 1] prefix offsets (row_off[N] = total tokens) and tok_row[t] = row
+// of packed token t (-1 past the end, up to NTmax).
+void launch_pack_rows(const int32_t* kv_len, int R, int nb, int NTmax, int32_t* row_off, int32_t* tok_row,
+                      hipStream_t s);
 // cvec[(k*nc + ci), :] = ct[k, :] + (spk ? (ci == 0 ? bs : spkproj[ci-1]) : 0)
 void launch_assemble_cvec(const float* ct, const float* bs, const float* spkproj, int S, int nc,
                           int d, float* cvec, hipStream_t s);

@@ -72,7 +72,7 @@ cfm_status check_config(const cfm_config* c) {
         // the matrix-core GEMMs address each operand with 32-bit byte offsets
         const long long es = c->dtype == CFM_BF16 ? 2 : 4;
         const long long P = c->cond_mode == CFM_COND_PREFIX ? c->n_prefix : 0;
-        const long long tokens = (long long)c->n_branches * c->max_requests * (c->max_frames + P);
+        const long long tokens = (long long)c->n_branches * c->max_requests * round8(c->max_frames + P);
         const long long wide = std::max<long long>(3LL * c->d_model, c->ffn_dim);
         const long long cond_rows = (long long)c->max_requests * (P > 0 ? P : c->max_frames);
         if (tokens * wide * es >= kMaxOperandBytes ||
@@ -169,7 +169,8 @@ Slot find(const Manifest& m, const char* name, long long col0 = 0) {
 }
 
 struct Layout {   // workspace regions, byte offsets
-    size_t h, act, big, vt, v, cproj, temb, tpre, ct, spkproj, cvec, mod, kvlen, kvalid, tfull, total;
+    size_t h, act, big, vt, v, cproj, temb, tpre, ct, spkproj, cvec, mod, kvlen, kvalid, tfull, rowoff, tokrow,
+        total;
 };
 
 inline long long round64(long long v) { return (v + 63) / 64 * 64; }
@@ -178,7 +179,11 @@ Layout plan_workspace(const cfm_config& c) {
     const size_t es = c.dtype == CFM_BF16 ? 2 : 4;
     const size_t Rm = c.max_requests, Tx = c.max_frames, S = c.max_steps;
     const size_t P = c.cond_mode == CFM_COND_PREFIX ? c.n_prefix : 0;
-    const size_t T = Tx + P, N = (size_t)c.n_branches * Rm, d = c.d_model;
+    const size_t N = (size_t)c.n_branches * Rm, d = c.d_model;
+    // packed layout of masked batches (bf16 path, frame-aligned condition): rows
+    // are rounded up to 8 tokens, so token buffers hold N * round8(T) tokens
+    const bool packable = c.dtype == CFM_BF16 && c.cond_mode == CFM_COND_CHANNEL;
+    const size_t T = Tx + P, TT = packable ? (T + 7) / 8 * 8 : T;
     const size_t Tc = c.cond_mode == CFM_COND_PREFIX ? P : Tx;
     const size_t nc = 1 + (c.spk_dim > 0 ? Rm : 0);
     const size_t ML = (6 * (size_t)c.n_layers + 2) * d;
@@ -186,9 +191,9 @@ Layout plan_workspace(const cfm_config& c) {
     Layout L;
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, 256); return o; };
-    L.h = take(N * T * d * 4);
-    L.act = take(N * T * d * es);
-    L.big = take(N * T * wide * es);
+    L.h = take(N * TT * d * 4);
+    L.act = take(N * TT * d * es);
+    L.big = take(N * TT * wide * es);
     // bf16 path: V transposed per head, [rows, H, 64, T rounded up to 64]
     L.vt = take(c.dtype == CFM_BF16 ? N * d * (size_t)round64(T) * 2 : 0);
     L.v = take(N * Tx * c.latent_dim * 4);
@@ -202,6 +207,8 @@ Layout plan_workspace(const cfm_config& c) {
     L.kvlen = take(Rm * 4);
     L.kvalid = take(Rm * (size_t)round64(T));           // per-key validity bytes
     L.tfull = take(Rm * (size_t)round64(T) / 64);       // per-64-key-tile "all valid" bytes
+    L.rowoff = take(packable ? (N + 1) * 4 : 0);
+    L.tokrow = take(packable ? N * TT * 4 : 0);
     L.total = off;
     return L;
 }
@@ -449,6 +456,18 @@ cfm_status cfm_sample(cfm_ctx* c, const float* x0, const float* cond, const floa
     int32_t* kvlen = wsp<int32_t>(c, ly.kvlen);
     uint8_t* kvalid = wsp<uint8_t>(c, ly.kvalid);
     uint8_t* tfull = wsp<uint8_t>(c, ly.tfull);
+    // A masked batch on the bf16 path runs packed: row b*R + r keeps only its
+    // first kv_len[r] frames (up to the last valid one) rounded up to 8 tokens,
+    // rows follow each other, and every token-parallel kernel works on the
+    // packed token count, read on the device. The outputs are those of the
+    // padded layout: every operation but attention is token-local, attention
+    // masks every key from kv_len on, and the frames cut off are masked keys
+    // whose velocities are never used.
+    const bool packed = bf && !prefix && frame_mask != nullptr;
+    const long long NTk = packed ? (long long)N * ((T + 7) / 8 * 8) : NT;   // token capacity
+    int32_t* rowoff = packed ? wsp<int32_t>(c, ly.rowoff) : nullptr;
+    int32_t* tokrow = packed ? wsp<int32_t>(c, ly.tokrow) : nullptr;
+    const int32_t* ntok = packed ? rowoff + N : nullptr;
 
     // GEMM through matrix cores (bf16 sampler) or fp32 FMA (fp32 sampler)
     auto gemm = [&](int cls, bool a_f32, const void* A, int lda, Slot w, int M, int Nn, int K, int epi,
@@ -473,6 +492,7 @@ cfm_status cfm_sample(cfm_ctx* c, const float* x0, const float* cond, const floa
     // ---- set-up, once per call
     timed(c, CFM_K_HOISTED, s, [&] {
         launch_key_prep(frame_mask, Tx, nullptr, R, P, T, Tp, kvlen, kvalid, tfull, s);
+        if (packed) launch_pack_rows(kvlen, R, nb, (int)NTk, rowoff, tokrow, s);
     });
     timed(c, CFM_K_HOISTED, s, [&] { launch_timestep_embedding(temb, S, g.t_freq_dim, s); });
     hoisted(false, temb, g.t_freq_dim, c->t1w, c->t1b, S, d, g.t_freq_dim, tpre, d);
@@ -498,6 +518,7 @@ cfm_status cfm_sample(cfm_ctx* c, const float* x0, const float* cond, const floa
         m.tokens_per_row = tokens_per_row;
         m.n_requests = R;
         m.spk_branch = spk_branch;
+        m.tok_row = tokrow;
         return m;
     };
     float w[3] = {1.0f, 0.0f, 0.0f};
@@ -507,7 +528,7 @@ cfm_status cfm_sample(cfm_ctx* c, const float* x0, const float* cond, const floa
     AttnParams ap;
     ap.qkv = big; ap.vt = vt; ap.Tp = Tp; ap.o = act; ap.rows = N; ap.T = T; ap.H = H; ap.hd = hd;
     ap.kv_len = kvlen; ap.kv_mod = R; ap.key_mask = frame_mask; ap.mask_stride = Tx; ap.P = P;
-    ap.kvalid = kvalid; ap.tile_full = tfull;
+    ap.kvalid = kvalid; ap.tile_full = tfull; ap.row_off = rowoff;
 
     // ---- Euler steps
     for (int k = 0; k < S; ++k) {
@@ -524,43 +545,50 @@ cfm_status cfm_sample(cfm_ctx* c, const float* x0, const float* cond, const floa
             ep.out = h; ep.ldo = d;
             ep.R = R; ep.Tx = Tx; ep.T = T; ep.P = P; ep.nb = nb; ep.cond_branch0 = cond0;
             ep.cproj = prefix ? nullptr : cproj;
+            ep.row_off = rowoff;
             gemm(CFM_K_GEMM_IN, true, out, C, c->inxw, R * Tx, d, C, EPI_INPROJ, ep);
         }
         for (int l = 0; l < L; ++l) {
             const auto& W = c->layers[l];
             const float* ml = modk + (long long)l * 6 * d;
             LnParams ln;
-            ln.h = h; ln.y = act; ln.d = d; ln.n_out = NT; ln.Tin = T; ln.Tout = T; ln.off = 0;
+            ln.h = h; ln.y = act; ln.d = d; ln.n_out = NTk; ln.Tin = T; ln.Tout = T; ln.off = 0;
             ln.shift = rowmod(ml + 0 * d, T); ln.scale = rowmod(ml + 1 * d, T); ln.out_bf16 = bf;
+            ln.n_dev = ntok;
             timed(c, CFM_K_ADALN, s, [&] { launch_adaln(ln, s); });
             EpiParams e1; e1.bias = wp<float>(c, W.qkvb); e1.out = big;
             if (bf) {   // q|k rows of 2d, v transposed per head for the attention tiles
                 e1.ldo = 2 * d; e1.vt = vt; e1.H = H; e1.T = T; e1.Tp = Tp; e1.d2 = 2 * d;
+                e1.tok_row = tokrow; e1.row_off = rowoff; e1.m_dev = ntok;
             } else {
                 e1.ldo = 3 * d;
             }
-            gemm(CFM_K_GEMM_QKV, false, act, d, W.qkvw, (int)NT, 3 * d, d, bf ? EPI_QKV : EPI_ACT, e1);
+            gemm(CFM_K_GEMM_QKV, false, act, d, W.qkvw, (int)NTk, 3 * d, d, bf ? EPI_QKV : EPI_ACT, e1);
             timed(c, CFM_K_ATTENTION, s, [&] {
                 if (bf) launch_attention_bf16(ap, s); else launch_attention_f32(ap, s);
             });
             EpiParams e2; e2.bias = wp<float>(c, W.projb); e2.out = h; e2.ldo = d; e2.gate = rowmod(ml + 2 * d, T);
-            gemm(CFM_K_GEMM_PROJ, false, act, d, W.projw, (int)NT, d, d, EPI_GATED, e2);
+            e2.m_dev = ntok;
+            gemm(CFM_K_GEMM_PROJ, false, act, d, W.projw, (int)NTk, d, d, EPI_GATED, e2);
             ln.shift = rowmod(ml + 3 * d, T); ln.scale = rowmod(ml + 4 * d, T);
             timed(c, CFM_K_ADALN, s, [&] { launch_adaln(ln, s); });
-            EpiParams e3; e3.bias = wp<float>(c, W.fc1b); e3.out = big; e3.ldo = f;
-            gemm(CFM_K_GEMM_FC1, false, act, d, W.fc1w, (int)NT, f, d, EPI_GELU_ACT, e3);
+            EpiParams e3; e3.bias = wp<float>(c, W.fc1b); e3.out = big; e3.ldo = f; e3.m_dev = ntok;
+            gemm(CFM_K_GEMM_FC1, false, act, d, W.fc1w, (int)NTk, f, d, EPI_GELU_ACT, e3);
             EpiParams e4; e4.bias = wp<float>(c, W.fc2b); e4.out = h; e4.ldo = d; e4.gate = rowmod(ml + 5 * d, T);
-            gemm(CFM_K_GEMM_FC2, false, big, f, W.fc2w, (int)NT, d, f, EPI_GATED, e4);
+            e4.m_dev = ntok;
+            gemm(CFM_K_GEMM_FC2, false, big, f, W.fc2w, (int)NTk, d, f, EPI_GATED, e4);
         }
         {
             const float* mf = modk + (long long)L * 6 * d;
             LnParams ln;
             ln.h = h; ln.y = act; ln.d = d; ln.n_out = (long long)N * Tx; ln.Tin = T; ln.Tout = Tx; ln.off = P;
             ln.shift = rowmod(mf, Tx); ln.scale = rowmod(mf + d, Tx); ln.out_bf16 = bf;
+            if (packed) { ln.n_out = NTk; ln.Tin = ln.Tout = 1; ln.n_dev = ntok; }   // tokens map one to one
             timed(c, CFM_K_ADALN, s, [&] { launch_adaln(ln, s); });
             EpiParams ep; ep.bias = wp<float>(c, c->outb); ep.out = vel; ep.ldo = C;
             ep.R = R; ep.Tx = Tx; ep.mask = frame_mask;
-            gemm(CFM_K_GEMM_OUT, false, act, d, c->outw, N * Tx, C, d, EPI_VOUT, ep);
+            ep.tok_row = tokrow; ep.row_off = rowoff; ep.m_dev = ntok;
+            gemm(CFM_K_GEMM_OUT, false, act, d, c->outw, packed ? (int)NTk : N * Tx, C, d, EPI_VOUT, ep);
         }
         timed(c, CFM_K_CFG_EULER, s, [&] {
             launch_cfg_euler(vel, nb, dt * w[0], dt * w[1], dt * w[2], frame_mask, R, Tx, C, out, s);

@@ -179,3 +179,26 @@ def test_fewer_requests_and_frames_than_capacity():
     a, _ = run_sampler(s, W, I, sampler=big)
     b, _ = run_sampler(s, W, I)
     np.testing.assert_array_equal(a, b)
+
+
+def test_mask_with_holes_and_ragged_rows_matches_oracle():
+    """Frame masks that are not a prefix (holes inside a request), a request with
+    no valid frame and one whose every frame is valid, at a frame count that is
+    not a multiple of 8: the masked keys are excluded from attention and the
+    masked frames keep x0, as in the oracle."""
+    s = reduced("varlen_masked").replace(n_frames=203, n_requests=4, varlen=(1, 203))
+    W, I = synth.make_weights(s, 371), synth.make_inputs(s, 372)
+    rng = np.random.default_rng(373)
+    mask = (rng.random((s.n_requests, s.n_frames)) > 0.3).astype(np.uint8)
+    mask[0, 150:] = 0
+    mask[1] = 0
+    mask[2] = 1
+    mask[3, :5] = 0
+    mask[3, 9:] = 0
+    got, _ = run_sampler(s, W, I, mask=mask)
+    want = O.sample(W, s, I["x0"], I["cond"], I["spk"], mask, s.n_steps, s.guidance)
+    valid = mask.astype(bool)
+    err = rel_l2(got, want, valid)
+    print(f"holes: rel-L2 {err:.3e}")
+    assert err <= TOL[s.dtype], err
+    np.testing.assert_array_equal(got[~valid], I["x0"][~valid])
