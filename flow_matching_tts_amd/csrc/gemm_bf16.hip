@@ -585,11 +585,12 @@ gemm_pp_kernel(const bf16* __restrict__ A, int lda, const bf16* __restrict__ W, 
     for (int st = 0; st < 3 && st < nk; ++st) issue(st);
     wait_stages(min(nk, 3) - 1);
     sync();
+    auto compute = [&] { mma_frags<C>(acc, f); };
     if (grp == 0) {
         for (int k = 0; k < nk; ++k) {
             mphase(k);
             sync();
-            mma_frags<C>(acc, f);
+            compute();
             wait_next(k);
             sync();
         }
@@ -599,7 +600,7 @@ gemm_pp_kernel(const bf16* __restrict__ A, int lda, const bf16* __restrict__ W, 
             mphase(k);
             wait_next(k);
             sync();
-            mma_frags<C>(acc, f);
+            compute();
             if (k + 1 < nk) sync();
         }
     }
