@@ -12,7 +12,9 @@ Prints ONE JSON line on stdout:
   frames           latent frame-steps/s and generated frames/s
   gemm_attn_frac   GEMM + attention FLOPs / their kernel time / 2.5 PFLOP/s (bf16 dense)
   roofline         the dominant kernel class: algorithmic FLOPs (or bytes) per launch /
-                   its mean launch duration (HIP events on the launch stream)
+                   its mean launch duration (HIP events on the launch stream); traffic =
+                   HBM-side bytes per launch from the committed rocprofv3 counter summary
+                   (profiles/traffic_mel_dit.txt), null once the GEMM sources differ
   cpu_baseline     the fp64 CPU oracle on a bounded sample of the same workload
 """
 from __future__ import annotations
@@ -79,6 +81,52 @@ def cpu_baseline(s, W, I, max_workers: int):
             "seconds": t}
 
 
+PROBE_BYTES = 1 << 30     # bytes read (and written) by one launch of the copy probe
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_mel_dit.txt")
+TRAFFIC_SOURCES = ["gemm_bf16.hip", "epilogue.h", "kernels.h", "common.h"]
+
+
+def traffic_probe():
+    """A plain device copy of PROBE_BYTES, three launches: the HBM counters of this kernel,
+    divided into the bytes it must move, give the scale of FETCH_SIZE and WRITE_SIZE."""
+    import torch
+    src = torch.ones(PROBE_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"probe": "copy", "bytes_read": PROBE_BYTES, "bytes_written": PROBE_BYTES}), flush=True)
+
+
+def sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, "flow_matching_tts_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel_class, workload):
+    """HBM bytes per launch of the kernel class, from the committed counter summary, or None
+    when there is none for this kernel and workload or the kernel sources changed since."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    with open(TRAFFIC_FILE) as fh:
+        for line in fh:
+            line = line.strip()
+            if line and not line.startswith("#") and "=" in line:
+                k, v = line.split("=", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_class") != kernel_class or kv.get("workload") != workload:
+        return None
+    if kv.get("sources_sha256") != sources_sha256():
+        return None
+    return float(kv["traffic_bytes_per_launch"])
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -88,7 +136,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-workers", type=int, default=16)
     ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="only copy a known number of bytes (calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
+    if args.traffic_probe:
+        traffic_probe()
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the sampler shards by request "
               f"with no communication during sampling, so a multi-GPU figure is not measured here.",
@@ -166,7 +219,8 @@ def main():
         peak = PEAK_BF16 if mfma else PEAK_HBM
         roofline = {"kernel_class": dom, "bound": "mfma" if mfma else "hbm",
                     "achieved": achieved / (1e12 if mfma else 1e9), "peak": peak / (1e12 if mfma else 1e9),
-                    "unit": "TFLOP/s" if mfma else "GB/s", "frac": achieved / peak, "traffic": None,
+                    "unit": "TFLOP/s" if mfma else "GB/s", "frac": achieved / peak,
+                    "traffic": measured_traffic(dom, s.name),
                     "mean_launch_us": mean_s * 1e6, "launches": n,
                     "work_per_launch": work}
         mf = sum(model[c][0] * model[c][1] for c in MFMA_CLASSES)
