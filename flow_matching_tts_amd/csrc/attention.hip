@@ -2,12 +2,12 @@
 //
 // bf16 path (head_dim 64): flash-style, one block = 8 waves = 256 queries of
 // one (row, head), 32 per wave, all sharing each K and V^T tile staged in LDS;
-// keys stream through double-buffered LDS tiles
+// keys stream through a ring of LDS tiles
 // of 64 with the online softmax recurrence (running max m, running sum l,
 // rescale of the partial output by exp(m_old - m_new)), so the T x T score
 // matrix never exists. V arrives already transposed per head (the QKV GEMM
-// epilogue writes it that way), so every LDS tile is filled with plain
-// 16-byte loads and stores.
+// epilogue writes it that way), so every LDS tile is 64 rows of 128 contiguous
+// bytes in HBM, loaded straight into LDS.
 //
 // MFMA mapping (v_mfma_f32_32x32x16_bf16, C[i][j] = sum_k A[i][k] B[k][j]):
 //   S^T = K Q^T : A = the K tile (rows = keys), B = Q^T held in registers for
@@ -19,9 +19,9 @@
 //                 query per lane); the k slots of that operand are a fixed
 //                 permutation of the tile's keys, and the V^T operand is read
 //                 from LDS in that same key order.
-// Occupancy is what hides latency here: the kernel is limited to 128 VGPRs so
-// that two 8-wave blocks share a CU (4 waves per SIMD), and tiles alternate
-// between two LDS buffers so one barrier per tile suffices.
+// The kernel is limited to 128 VGPRs so that two 8-wave blocks share a CU (4
+// waves per SIMD); one barrier per tile suffices because the ring has a slot
+// more than the tiles in flight.
 // Masked keys are zero-filled in K and V and get a -inf score bias, so a
 // non-finite value behind a padded frame can never reach a valid output; tiles
 // whose 64 keys are all valid skip the bias. The 1/sqrt(hd) scale is folded into
@@ -37,19 +37,279 @@ namespace {
 
 constexpr int HD = 64;
 constexpr int KT = 64;         // keys per LDS tile
-constexpr int KP = HD + 8;     // K tile row pitch (bf16): 144 B
-constexpr int VP = KT + 8;     // V^T tile row pitch (bf16): 144 B
 // The running max is only moved when a tile's max exceeds it by more than
 // 2^8 in probability (8 in base-2 exponent): until then p = 2^(s - m) <= 256,
 // far from overflow in fp32 and in bf16, and softmax does not depend on the
 // constant subtracted, so skipping the rescale changes nothing but rounding.
 constexpr float RESCALE_SLACK = 8.0f;
+constexpr int OOB = 0x7ffffff0;   // buffer offset past every range: the load returns zeros
 
-__device__ __forceinline__ bool key_valid(const AttnParams& p, const uint8_t* km, int key, int kvl) {
-    if (key >= kvl) return false;
-    if (km == nullptr || key < p.P) return true;
-    return km[key - p.P] != 0;
+// LDS tile = 64 rows (keys of K, head dims of V^T) of 128 data bytes at a
+// 144-byte stride: the 16 rows that 16 lanes read at one chunk (one 128-bit
+// LDS read cycle) fall on 16 distinct bank groups, and every fragment read
+// is a per-lane base plus an immediate offset. Tiles arrive by direct
+// buffer-to-LDS loads: one load instruction fills 1 KiB at M0 + 16 * lane, so
+// instruction g covers rows 7g .. 7g + 6 (9 lanes per row: 8 data chunks and the
+// pad chunk) at M0 = 7g * 144, and its last lane rewrites the first chunk of
+// row 7g + 7 with the same data the next instruction brings. Ten instructions
+// cover a tile; the last spills past row 63 into a slack area nobody reads.
+constexpr int RS = 144;                    // row stride, bytes
+constexpr int GRP = 7;                     // rows per load instruction
+constexpr int NLD = (KT + GRP - 1) / GRP;  // load instructions per tile (10)
+constexpr int TILE_B = NLD * GRP * RS + 1024 - GRP * RS;   // bytes per tile incl. slack (10096)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t arsrc(const void* p, long long bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0,
+                                             (int)min(bytes, (long long)0x7fffffff), 0x00020000);
 }
+// buffer_load_dwordx4 ... lds: 16 bytes per lane land at M0 + 16 * lane
+__device__ __forceinline__ void adma16(__amdgpu_buffer_rsrc_t rs, int voff, unsigned lds_addr) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :: "s"(lds_addr), "v"(voff), "s"(rs) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void await_vm() { asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory"); }
+__device__ __forceinline__ void abarrier() { asm volatile("s_barrier" ::: "memory"); }
+
+template <int NW> struct AttnCfg {
+    static constexpr int NS = NW == 1 ? 2 : 3;                       // ring slots
+    static constexpr int PER = (2 * NLD + NW - 1) / NW;               // load instructions per wave per tile
+    static constexpr int SLOT_B = 2 * TILE_B + 1024;                  // K tile, V^T tile, 1 KiB sink
+    static constexpr int RING_B = NS * SLOT_B;
+};
+
+template <int NW>
+size_t attn_lds_bytes(int Tp) {
+    using A = AttnCfg<NW>;
+    return (size_t)A::RING_B + (size_t)A::NS * KT * 4 + (size_t)Tp + (size_t)Tp / KT;
+}
+
+// NW waves per block (8: 256 queries), 32 queries each, all sharing every
+// K / V^T tile; sequences of one tile use attn_short_kernel instead.
+//
+// K and V^T tiles go from HBM straight into an LDS ring of NS slots, issued
+// NS - 1 tiles ahead and awaited with explicit vmcnt waits, so the loop holds
+// no staging registers. K rows of keys at or past the row's key length are out
+// of the load's range and arrive as zeros. A tile that is not entirely valid
+// (tail or mask holes) is then patched in LDS: the K rows and V^T columns of its
+// invalid keys are zeroed and their score bias set to -inf, so a non-finite
+// value behind a masked key never reaches a valid output.
+template <int NW>
+__global__ void __launch_bounds__(64 * NW, 4)   // 4 waves per SIMD
+attn_bf16_kernel(AttnParams p) {
+    using A = AttnCfg<NW>;
+    constexpr int QT = 32 * NW;    // queries per block
+    constexpr int NT = 64 * NW;
+    constexpr int NS = A::NS, PER = A::PER;
+    extern __shared__ __attribute__((aligned(16))) char asmem[];
+    float* const kbias = (float*)(asmem + A::RING_B);               // NS x 64
+    uint8_t* const kvs = (uint8_t*)(kbias + NS * KT);               // Tp validity bytes, then tile flags
+    const unsigned ring_addr = (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)asmem;
+
+    const int row = blockIdx.z, head = blockIdx.y;
+    // the wave index picks the load instructions: keep it in a scalar register
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int j = lane & 31, h = lane >> 5;
+    // first token of the row and its length: padded rows hold T tokens each,
+    // packed rows row_off[row + 1] - row_off[row]
+    long long rbase;
+    int T;
+    if (p.row_off) {
+        rbase = p.row_off[row];
+        T = p.row_off[row + 1] - (int)rbase;
+        if (blockIdx.x * QT >= T) return;     // block-uniform: no query of this block exists
+    } else {
+        rbase = (long long)row * p.T;
+        T = p.T;
+    }
+    const int d = p.H * HD;
+    const long long ldk = 2LL * d;
+    const bf16* qbase = (const bf16*)p.qkv + rbase * ldk + head * HD;
+    const bf16* kbase = qbase + d;
+    const bf16* vtbase = (const bf16*)p.vt + (long long)(row * p.H + head) * HD * p.Tp;
+    const int q = blockIdx.x * QT + wave * 32 + j;
+
+    const int rr = row % p.kv_mod;
+    const int kvl = min(p.kv_len[rr], T);
+    const int ntiles = (kvl + KT - 1) / KT;
+    const int Tp = p.Tp;
+
+    bf16x8 qf[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+        qf[kk] = q < T ? *(const bf16x8*)(qbase + (long long)q * ldk + kk * 16 + h * 8) : bf16x8{};
+    // key validity and per-tile "all valid" flags into LDS (read while patching)
+    {
+        const uint8_t* kv = p.kvalid + (long long)rr * Tp;
+        const uint8_t* tf = p.tile_full + (long long)rr * (Tp / KT);
+        for (int i = tid; i < ntiles * KT / 16; i += NT) ((uint4*)kvs)[i] = ((const uint4*)kv)[i];
+        for (int i = tid; i < ntiles; i += NT) kvs[Tp + i] = tf[i];
+    }
+    // drain every load above with a wait the compiler sees: its bookkeeping then
+    // knows q is resident and puts no vmcnt wait inside the loop (such a wait
+    // would also wait for the ring's loads, which it does not see)
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    // K rows past the key length are out of range: they load as zeros
+    const __amdgpu_buffer_rsrc_t rk = arsrc(kbase, kvl > 0 ? ((long long)(kvl - 1) * ldk + HD) * 2 : 0);
+    const __amdgpu_buffer_rsrc_t rv = arsrc(vtbase, (long long)HD * Tp * 2);
+    const int lrow = lane / 9, lchunk = lane - 9 * (lane / 9);   // this lane's row / chunk in a load
+    auto issue = [&](int it) {
+        const unsigned slot = ring_addr + (unsigned)((it % NS) * A::SLOT_B);
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int g = wave * PER + i;             // load instruction (uniform): 0..9 K, 10..19 V^T, 20+ none
+            if (g >= 2 * NLD) {
+                if constexpr (NW > 1) adma16(rv, OOB, slot + 2 * TILE_B);   // keeps every wave's count equal
+                continue;
+            }
+            const bool isk = g < NLD;
+            const int gg = isk ? g : g - NLD;
+            const int r = gg * GRP + lrow;            // tile row
+            const bool ok = r < KT && lchunk < 8;
+            const unsigned dst = slot + (isk ? 0u : (unsigned)TILE_B) + (unsigned)(gg * GRP * RS);
+            if (isk) {
+                const int key = it * KT + r;
+                adma16(rk, ok && key < kvl ? (int)(((long long)key * ldk + lchunk * 8) * 2) : OOB, dst);
+            } else {
+                adma16(rv, ok ? (int)(((long long)r * Tp + it * KT + lchunk * 8) * 2) : OOB, dst);
+            }
+        }
+    };
+    auto wait_tiles = [&](int later) {   // this wave's loads done but those of `later` younger tiles
+        if constexpr (NS >= 3) { if (later >= 2) { await_vm<2 * PER>(); return; } }
+        if (later == 1) await_vm<PER>();
+        else await_vm<0>();
+    };
+
+    const float sl2 = 1.4426950408889634f / sqrtf((float)HD);   // 1/sqrt(hd) in base-2 units
+    f32x16 oacc[2] = {f32x16{}, f32x16{}};
+    // running max of the scaled scores (base 2); finite start so that a tile with
+    // no valid key (all scores -inf) gives exp2(-inf) = 0, never inf - inf
+    float m_run = -1e30f;
+    float l_part = 0.0f;
+    // per-lane fragment bases: K row j at chunk h, V^T row j at half h
+    const int kl = j * RS + h * 16, vl = TILE_B + j * RS + h * 8;
+
+    for (int it = 0; it < NS - 1 && it < ntiles; ++it) issue(it);
+    for (int it = 0; it < ntiles; ++it) {
+        const int cur = it % NS;
+        wait_tiles(min(ntiles - 1, it + NS - 2) - it);
+        abarrier();   // tile it is in LDS for every wave; slot (it - 1) % NS is free
+        const bool full = kvs[Tp + it] != 0;
+        const char* sb = asmem + cur * A::SLOT_B;
+        if (!full) {
+            // patch: zero the K rows and V^T columns of invalid keys, set their bias
+            char* ks = (char*)sb;
+            char* vt = ks + TILE_B;
+            const uint8_t* kv = kvs + it * KT;
+            for (int e = tid; e < KT * 8; e += NT) {
+                const int r = e >> 3, c = e & 7;      // K: key r, chunk c; V^T: head dim r, keys 8c .. 8c + 7
+                if (!kv[r]) *(bf16x8*)(ks + r * RS + c * 16) = bf16x8{};
+                bf16x8* vp = (bf16x8*)(vt + r * RS + c * 16);
+                const uint64_t okb = *(const uint64_t*)(kv + 8 * c);
+                if (okb != 0x0101010101010101ull) {
+                    bf16x8 vv = *vp;
+#pragma unroll
+                    for (int u = 0; u < 8; ++u)
+                        if (((okb >> (8 * u)) & 0xff) == 0) vv[u] = (bf16)0.0f;
+                    *vp = vv;
+                }
+            }
+            for (int e = tid; e < KT; e += NT) kbias[cur * KT + e] = kv[e] ? 0.0f : -INFINITY;
+            __syncthreads();
+        }
+        if (it + NS - 1 < ntiles) issue(it + NS - 1);
+
+        // S^T = K Q^T: s[kh][g*4 + r] = score(key kh*32 + 8g + 4h + r, query q)
+        const char* kb0 = sb + kl;
+        f32x16 s[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const bf16x8 a = *(const bf16x8*)(kb0 + kh * 32 * RS + kk * 32);
+                s[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[kh], 0, 0, 0);
+            }
+        if (!full) {   // partial tile: masked keys get -inf
+            const float* kbp = kbias + cur * KT;
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) s[kh][g * 4 + r] += kbp[kh * 32 + 8 * g + 4 * h + r];
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kh][i]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sl2;
+        // move the running max only when the tile max clears it by the slack
+        const bool move = mx > m_run + RESCALE_SLACK;
+        if (__any(move)) {   // some lane of the wave moves its max
+            const float m_new = move ? mx : m_run;
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 1 for lanes that keep their max
+            l_part *= alpha;
+            oacc[0] *= alpha;
+            oacc[1] *= alpha;
+            m_run = m_new;
+        }
+        float ls = 0.0f;
+        bf16x8 pb[2][2];
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float pv = __builtin_amdgcn_exp2f(fmaf(s[kh][g * 4 + r], sl2, -m_run));
+                    ls += pv;
+                    pb[kh][g >> 1][(g & 1) * 4 + r] = (bf16)pv;
+                }
+        l_part += ls;
+
+        // O^T += V^T P^T. B-operand slot e of lane half h (k-step ss of key half kh)
+        // is key kh*32 + 16 ss + 4h + e (e < 4) or kh*32 + 16 ss + 8 + 4h + (e - 4).
+        const char* vb0 = sb + vl;
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+                for (int ss = 0; ss < 2; ++ss) {
+                    const char* vr = vb0 + dt * 32 * RS + (kh * 32 + 16 * ss) * 2;
+                    const bf16x4 lo = *(const bf16x4*)(vr);
+                    const bf16x4 hi = *(const bf16x4*)(vr + 16);
+                    bf16x8 a;
+                    a[0] = lo[0]; a[1] = lo[1]; a[2] = lo[2]; a[3] = lo[3];
+                    a[4] = hi[0]; a[5] = hi[1]; a[6] = hi[2]; a[7] = hi[3];
+                    oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kh][ss], oacc[dt], 0, 0, 0);
+                }
+        // no barrier here: this slot is refilled only after a later iteration's
+        // barrier, which every wave reaches after these reads
+    }
+
+    const float l = l_part + __shfl_xor(l_part, 32, 64);
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    if (q < T) {
+        bf16* dst = (bf16*)p.o + (rbase + q) * d + head * HD;
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                bf16x4 o4;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) o4[r] = (bf16)(oacc[dt][g * 4 + r] * inv);
+                *(bf16x4*)(dst + dt * 32 + 8 * g + 4 * h) = o4;
+            }
+    }
+}
+
+constexpr int KP = HD + 8;     // short kernel: K tile row pitch (bf16), 144 B
+constexpr int VP = KT + 8;     // short kernel: V^T tile row pitch (bf16), 144 B
 
 // One KV tile in registers on its way to LDS: KV_CH chunks of K (one key, 8
 // head dims each) and of V^T (one head dim, 8 keys each) per thread, with the
@@ -91,11 +351,12 @@ struct KvStage {
     }
 };
 
-// NW waves per block, 32 queries each, all sharing every K / V^T tile: 8 for
-// long sequences; 1 for short ones (a block per 32 queries, no idle waves).
+// Short sequences (one key tile, T <= 64): one wave per 32 queries, the tile
+// staged through registers into a padded LDS layout (72-element rows) in one
+// step; with a single tile there is nothing to prefetch.
 template <int NW>
 __global__ void __launch_bounds__(64 * NW, 4)   // 4 waves per SIMD
-attn_bf16_kernel(AttnParams p) {
+attn_short_kernel(AttnParams p) {
     constexpr int QT = 32 * NW;    // queries per block
     constexpr int NT = 64 * NW;
     __shared__ __attribute__((aligned(16))) bf16 Ks[2][KT * KP];
@@ -239,6 +500,13 @@ attn_bf16_kernel(AttnParams p) {
     }
 }
 
+
+__device__ __forceinline__ bool key_valid(const AttnParams& p, const uint8_t* km, int key, int kvl) {
+    if (key >= kvl) return false;
+    if (km == nullptr || key < p.P) return true;
+    return km[key - p.P] != 0;
+}
+
 constexpr int FQ = 64;          // queries per block on the fp32 path
 constexpr int FKT = 64;         // keys per LDS tile on the fp32 path
 
@@ -307,14 +575,24 @@ attn_f32_kernel(AttnParams p) {
 
 }  // namespace
 
+template <int NW>
+void launch_attn_nw(const AttnParams& p, hipStream_t s) {
+    static const bool attr = [] {
+        return hipFuncSetAttribute((const void*)attn_bf16_kernel<NW>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                   160 * 1024) == hipSuccess;
+    }();
+    (void)attr;
+    dim3 grid((p.T + 32 * NW - 1) / (32 * NW), p.H, p.rows);
+    attn_bf16_kernel<NW><<<grid, 64 * NW, attn_lds_bytes<NW>(p.Tp), s>>>(p);
+}
+
 void launch_attention_bf16(const AttnParams& p, hipStream_t s) {
     if (p.rows <= 0 || p.T <= 0) return;
     if (p.T <= 64) {
         dim3 grid((p.T + 31) / 32, p.H, p.rows);
-        attn_bf16_kernel<1><<<grid, 64, 0, s>>>(p);
+        attn_short_kernel<1><<<grid, 64, 0, s>>>(p);
     } else {
-        dim3 grid((p.T + 255) / 256, p.H, p.rows);
-        attn_bf16_kernel<8><<<grid, 512, 0, s>>>(p);
+        launch_attn_nw<8>(p, s);
     }
 }
 
