@@ -626,6 +626,166 @@ void launch_pp(const bf16* A, int lda, const bf16* W, int ldw, int M, int N, int
     gemm_pp_kernel<C, EPI><<<tm * tn, C::NT, C::LDS_BYTES, s>>>(A, lda, W, ldw, M, N, K, tm, tn, ep);
 }
 
+// Ping-pong with K stage 64 (tile 14): 128-byte LDS rows (one cache line per
+// row per stage, eight rows per load instruction), a 2-slot ring of 64 KiB
+// slots, and phases of 32 MFMAs, so a barrier pair is paid per 64 of K instead
+// of 32. Only group 0 issues loads: stage j is issued in group 0's M(j - 1),
+// after the barrier that ends group 1's reads of stage j - 2 (same slot), and
+// awaited at the end of its C(j - 1), before the barrier that publishes it
+// (two phases of latency). Group 1 issues no loads and never waits on vmcnt.
+constexpr int BK64 = 64;
+
+__device__ __forceinline__ int swz64(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
+
+// One operand's share of a K-64 stage: INSTR loads of 8 rows each. Per lane
+// only the row base and the swizzled chunk are kept (the swizzle of a row group
+// alternates between two patterns, c and c ^ 4); everything else is uniform.
+template <int INSTR>
+__device__ __forceinline__ void dma_stage64(__amdgpu_buffer_rsrc_t rs, int ld, int rows_total, int K, int r0,
+                                            int k0, unsigned slot_addr, int w4, int lane) {
+    const int lr = lane >> 3;                              // row within a group
+    const int c0 = (lane & 7) ^ (lane >> 4);               // chunk fetched in even groups (odd: c0 ^ 4)
+    const int g0 = w4 * INSTR;                             // first group of this wave (uniform)
+    const int rbase = (r0 + g0 * 8 + lr) * ld * 2;        // byte offset of this lane's row in group g0
+    const int rows_left = rows_total - r0 - g0 * 8 - lr;   // rows of this lane's column still in range
+    const int k_left = K - k0;
+#pragma unroll
+    for (int i = 0; i < INSTR; ++i) {
+        const int c = ((g0 + i) & 1) ? (c0 ^ 4) : c0;
+        const bool ok = i * 8 < rows_left && c * 8 < k_left;
+        const int off = ok ? rbase + i * 8 * ld * 2 + (k0 + c * 8) * 2 : OOB;
+        dma16(rs, off, __builtin_amdgcn_readfirstlane(slot_addr + (g0 + i) * 8 * BK64 * 2));
+    }
+}
+
+template <typename C> struct Frags64 {
+    bf16x8 a[BK64 / 16][C::TM], b[BK64 / 16][C::TN];
+};
+
+template <typename C>
+__device__ __forceinline__ void read_frags64(Frags64<C>& f, const bf16* as, const bf16* ws, int wm, int wn, int li,
+                                             int lh) {
+#pragma unroll
+    for (int ks = 0; ks < BK64 / 16; ++ks) {
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i) {
+            const int row = wm * C::WM + i * 32 + li;
+            f.a[ks][i] = *(const bf16x8*)(as + row * BK64 + swz64(row, ks * 2 + lh) * 8);
+        }
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j) {
+            const int row = wn * C::WN + j * 32 + li;
+            f.b[ks][j] = *(const bf16x8*)(ws + row * BK64 + swz64(row, ks * 2 + lh) * 8);
+        }
+    }
+}
+
+template <typename C, int EPI>
+__global__ void __launch_bounds__(C::NT)
+gemm_pp64_kernel(const bf16* __restrict__ A, int lda, const bf16* __restrict__ W, int ldw,
+                 int M, int N, int K, int tm, int tn, EpiParams ep) {
+    static_assert(C::WGM == 2 && C::WGN == 4, "two groups of four waves");
+    constexpr int SLOT = (C::BM + C::BN) * BK64;                // bf16 elements
+    constexpr int AI = C::BM / 8 / 4, WI = C::BN / 8 / 4;       // loads per group-0 wave per stage
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    bf16* const ring = (bf16*)smem;
+    const unsigned ring_addr = (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)smem;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int li = lane & 31, lh = lane >> 5;
+    // the group decides control flow around barriers: make it provably wave-uniform
+    const int grp = __builtin_amdgcn_readfirstlane(wave) / C::WGN, wn = wave % C::WGN;
+    int mt, nt;
+    tile_of(blockIdx.x, tm * tn, tm, tn, mt, nt);
+    const int m0 = mt * C::BM, n0 = nt * C::BN;
+    if (ep.m_dev) {
+        M = min(M, *ep.m_dev);
+        if (m0 >= M) return;   // whole block, before any barrier
+    }
+    const __amdgpu_buffer_rsrc_t ra = rsrc_of(A, (long long)M * lda * 2);
+    const __amdgpu_buffer_rsrc_t rw = rsrc_of(W, (long long)N * ldw * 2);
+    const int nk = (K + BK64 - 1) / BK64;
+
+    f32x16 acc[C::TM][C::TN];
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j) acc[i][j] = f32x16{};
+
+    auto issue = [&](int stage) {   // group 0 only: wn = 0..3 splits the rows
+        const unsigned slot = ring_addr + (unsigned)((stage & 1) * SLOT * 2);
+        dma_stage64<AI>(ra, lda, M, K, m0, stage * BK64, slot, wn, lane);
+        dma_stage64<WI>(rw, ldw, N, K, n0, stage * BK64, slot + C::BM * BK64 * 2, wn, lane);
+    };
+    auto sync = [&] {
+        __builtin_amdgcn_sched_barrier(0);
+        barrier_only();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    Frags64<C> f;
+    auto mphase = [&](int k) {
+        const bf16* sl = ring + (k & 1) * SLOT;
+        read_frags64<C>(f, sl, sl + C::BM * BK64, grp, wn, li, lh);
+        if (grp == 0 && k >= 1 && k + 1 < nk) issue(k + 1);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    };
+    auto compute = [&] {
+#pragma unroll
+        for (int ks = 0; ks < BK64 / 16; ++ks)
+#pragma unroll
+            for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+                for (int j = 0; j < C::TN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[ks][i], f.b[ks][j], acc[i][j], 0, 0, 0);
+    };
+
+    if (grp == 0) {
+        issue(0);
+        if (nk > 1) { issue(1); wait_vm<AI + WI>(); } else { wait_vm<0>(); }
+    }
+    sync();
+    if (grp == 0) {
+        for (int k = 0; k < nk; ++k) {
+            mphase(k);
+            sync();
+            compute();
+            if (k + 1 < nk) wait_vm<0>();   // stage k + 1 (the only one in flight) has landed
+            sync();
+        }
+    } else {
+        for (int k = 0; k < nk; ++k) {
+            if (k == 0) sync();
+            mphase(k);
+            sync();
+            compute();
+            if (k + 1 < nk) sync();
+        }
+    }
+    wait_vm<0>();
+    __syncthreads();
+    float* wl = (float*)smem + wave * EPI_WAVE_FLOATS;
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j)
+            epi_block<EPI>(ep, acc[i][j], wl, m0 + grp * C::WM + i * 32, n0 + wn * C::WN + j * 32, M, N, lane);
+}
+
+template <typename C, int EPI>
+void launch_pp64(const bf16* A, int lda, const bf16* W, int ldw, int M, int N, int K,
+                 const EpiParams& ep, hipStream_t s) {
+    const int tn = (N + C::BN - 1) / C::BN, tm = (M + C::BM - 1) / C::BM;
+    constexpr int LDS = 2 * (C::BM + C::BN) * BK64 * 2;
+    static_assert(LDS >= C::NW * EPI_WAVE_FLOATS * 4, "epilogue staging fits in the ring");
+    static const bool attr = [] {
+        return hipFuncSetAttribute((const void*)gemm_pp64_kernel<C, EPI>,
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, LDS) == hipSuccess;
+    }();
+    (void)attr;
+    gemm_pp64_kernel<C, EPI><<<tm * tn, C::NT, LDS, s>>>(A, lda, W, ldw, M, N, K, tm, tn, ep);
+}
+
 template <typename C, int EPI>
 void launch_dcfgp(const bf16* A, int lda, const bf16* W, int ldw, int M, int N, int K,
                   const EpiParams& ep, hipStream_t s) {
@@ -678,7 +838,7 @@ void launch_epi(int tile, const AT* A, int lda, const bf16* W, int ldw, int M, i
             // 128x128 tiles, whose fixed cost is lower, win)
             const long long big = (long long)((M + 255) / 256) * ((N + 255) / 256);
             const long long mid = (long long)((M + 127) / 128) * ((N + 127) / 128);
-            tile = big >= 192 ? (N >= 1024 || K >= 1024 ? 13 : 1) : mid >= 160 ? 6 : 10;
+            tile = big >= 192 ? (N >= 1024 || K >= 1024 ? (EPI == EPI_QKV ? 13 : 14) : 1) : mid >= 160 ? 6 : 10;
         }
         switch (tile) {
             case 2: launch_cfg<C2, AT, EPI>(A, lda, W, ldw, M, N, K, ep, s); break;
@@ -693,6 +853,7 @@ void launch_epi(int tile, const AT* A, int lda, const bf16* W, int ldw, int M, i
             case 11: launch_dcfgp<D8P, EPI>(A, lda, W, ldw, M, N, K, ep, s); break;
             case 12: launch_dcfgp<D9P, EPI>(A, lda, W, ldw, M, N, K, ep, s); break;
             case 13: launch_pp<D9, EPI>(A, lda, W, ldw, M, N, K, ep, s); break;
+            case 14: launch_pp64<D9, EPI>(A, lda, W, ldw, M, N, K, ep, s); break;
             default: launch_cfg<C1, AT, EPI>(A, lda, W, ldw, M, N, K, ep, s); break;
         }
     }

@@ -624,7 +624,7 @@ cfm_status cfm_gemm_bf16(const void* A, int a_is_f32, int lda, const void* W, in
                          const float* bias, int M, int N, int K, int epilogue,
                          const float* gate, void* C, int ldc, int tile, void* stream) {
     if (M < 0 || N < 0 || K < 0) return fail(CFM_E_VALUE, "negative size");
-    if (tile < 0 || tile > 13 || (tile > 1 && a_is_f32)) return fail(CFM_E_VALUE, "tile %d", tile);
+    if (tile < 0 || tile > 14 || (tile > 1 && a_is_f32)) return fail(CFM_E_VALUE, "tile %d", tile);
     if (epilogue < 0 || epilogue > 3) return fail(CFM_E_VALUE, "epilogue %d", epilogue);
     if (M == 0 || N == 0) return CFM_OK;
     if (A == nullptr || W == nullptr || C == nullptr) return fail(CFM_E_NULL, "A, W or C is NULL");
