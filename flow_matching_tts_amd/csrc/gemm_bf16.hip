@@ -834,11 +834,11 @@ void launch_epi(int tile, const AT* A, int lda, const bf16* W, int ldw, int M, i
     } else {
         if (tile == 0) {
             // the largest tile that still gives about one tile per CU or more; 256x256
-            // tiles run the ping-pong kernel, unless N and K are both small (then
+            // tiles run the K-64 ping-pong kernel, unless N and K are both small (then
             // 128x128 tiles, whose fixed cost is lower, win)
             const long long big = (long long)((M + 255) / 256) * ((N + 255) / 256);
             const long long mid = (long long)((M + 127) / 128) * ((N + 127) / 128);
-            tile = big >= 192 ? (N >= 1024 || K >= 1024 ? (EPI == EPI_QKV ? 13 : 14) : 1) : mid >= 160 ? 6 : 10;
+            tile = big >= 192 ? (N >= 1024 || K >= 1024 ? 14 : 1) : mid >= 160 ? 6 : 10;
         }
         switch (tile) {
             case 2: launch_cfg<C2, AT, EPI>(A, lda, W, ldw, M, N, K, ep, s); break;
