@@ -604,8 +604,11 @@ gemm_pp_kernel(const bf16* __restrict__ A, int lda, const bf16* __restrict__ W, 
             if (k + 1 < nk) sync();
         }
     }
+    // No block barrier before the epilogue: after its last barrier no wave reads
+    // the ring again (group 1's last multiply works from registers) and no load is
+    // in flight, so group 0 stages its output in its own 4 KiB area at once,
+    // while group 1 is still multiplying.
     wait_vm<0>();
-    __syncthreads();
     float* wl = (float*)smem + wave * EPI_WAVE_FLOATS;
 #pragma unroll
     for (int i = 0; i < C::TM; ++i)
@@ -629,10 +632,13 @@ void launch_pp(const bf16* A, int lda, const bf16* W, int ldw, int M, int N, int
 // Ping-pong with K stage 64 (tile 14): 128-byte LDS rows (one cache line per
 // row per stage, eight rows per load instruction), a 2-slot ring of 64 KiB
 // slots, and phases of 32 MFMAs, so a barrier pair is paid per 64 of K instead
-// of 32. Only group 0 issues loads: stage j is issued in group 0's M(j - 1),
-// after the barrier that ends group 1's reads of stage j - 2 (same slot), and
-// awaited at the end of its C(j - 1), before the barrier that publishes it
-// (two phases of latency). Group 1 issues no loads and never waits on vmcnt.
+// of 32. Each wave loads 1/8 of every stage. Group 0 issues its part of stage
+// j at the start of its M(j - 1) (after the barrier that ends group 1's reads
+// of stage j - 2, same slot) and awaits it at the end of its C(j - 1); group 1
+// issues its part of stage j at the end of its M(j - 2), once its own reads of
+// stage j - 2 are complete (group 0 read that slot a phase earlier), and awaits
+// it at the end of its M(j - 1). Both waits come before the barrier after which
+// group 0 reads stage j, and both leave two phases for the loads to land.
 constexpr int BK64 = 64;
 
 __device__ __forceinline__ int swz64(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
@@ -686,7 +692,8 @@ gemm_pp64_kernel(const bf16* __restrict__ A, int lda, const bf16* __restrict__ W
                  int M, int N, int K, int tm, int tn, EpiParams ep) {
     static_assert(C::WGM == 2 && C::WGN == 4, "two groups of four waves");
     constexpr int SLOT = (C::BM + C::BN) * BK64;                // bf16 elements
-    constexpr int AI = C::BM / 8 / 4, WI = C::BN / 8 / 4;       // loads per group-0 wave per stage
+    constexpr int AI = C::BM / 8 / C::NW, WI = C::BN / 8 / C::NW;   // loads per wave per stage
+    constexpr int L = AI + WI;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     bf16* const ring = (bf16*)smem;
     const unsigned ring_addr = (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)smem;
@@ -713,10 +720,10 @@ gemm_pp64_kernel(const bf16* __restrict__ A, int lda, const bf16* __restrict__ W
 #pragma unroll
         for (int j = 0; j < C::TN; ++j) acc[i][j] = f32x16{};
 
-    auto issue = [&](int stage) {   // group 0 only: wn = 0..3 splits the rows
+    auto issue = [&](int stage) {   // this wave's 1/8 of the stage's rows
         const unsigned slot = ring_addr + (unsigned)((stage & 1) * SLOT * 2);
-        dma_stage64<AI>(ra, lda, M, K, m0, stage * BK64, slot, wn, lane);
-        dma_stage64<WI>(rw, ldw, N, K, n0, stage * BK64, slot + C::BM * BK64 * 2, wn, lane);
+        dma_stage64<AI>(ra, lda, M, K, m0, stage * BK64, slot, wave, lane);
+        dma_stage64<WI>(rw, ldw, N, K, n0, stage * BK64, slot + C::BM * BK64 * 2, wave, lane);
     };
     auto sync = [&] {
         __builtin_amdgcn_sched_barrier(0);
@@ -724,10 +731,9 @@ gemm_pp64_kernel(const bf16* __restrict__ A, int lda, const bf16* __restrict__ W
         __builtin_amdgcn_sched_barrier(0);
     };
     Frags64<C> f;
-    auto mphase = [&](int k) {
+    auto reads = [&](int k) {
         const bf16* sl = ring + (k & 1) * SLOT;
         read_frags64<C>(f, sl, sl + C::BM * BK64, grp, wn, li, lh);
-        if (grp == 0 && k >= 1 && k + 1 < nk) issue(k + 1);
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     };
     auto compute = [&] {
@@ -740,30 +746,37 @@ gemm_pp64_kernel(const bf16* __restrict__ A, int lda, const bf16* __restrict__ W
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[ks][i], f.b[ks][j], acc[i][j], 0, 0, 0);
     };
 
-    if (grp == 0) {
-        issue(0);
-        if (nk > 1) { issue(1); wait_vm<AI + WI>(); } else { wait_vm<0>(); }
-    }
+    issue(0);
+    if (nk > 1) { issue(1); wait_vm<L>(); } else { wait_vm<0>(); }
     sync();
     if (grp == 0) {
         for (int k = 0; k < nk; ++k) {
-            mphase(k);
+            if (k >= 1 && k + 1 < nk) issue(k + 1);   // first: needed by the end of the next phase
+            reads(k);
             sync();
             compute();
-            if (k + 1 < nk) wait_vm<0>();   // stage k + 1 (the only one in flight) has landed
+            if (k + 1 < nk) wait_vm<0>();   // this wave's part of stage k + 1 has landed
             sync();
         }
     } else {
         for (int k = 0; k < nk; ++k) {
             if (k == 0) sync();
-            mphase(k);
+            reads(k);                       // complete before the slot is refilled below
+            if (k + 2 < nk) issue(k + 2);
+            if (k + 1 < nk) {               // this wave's part of stage k + 1 has landed
+                if (k + 2 < nk) wait_vm<L>();
+                else wait_vm<0>();
+            }
             sync();
             compute();
             if (k + 1 < nk) sync();
         }
     }
+    // No block barrier before the epilogue: after its last barrier no wave reads
+    // the ring again (group 1's last multiply works from registers) and no load is
+    // in flight, so group 0 stages its output in its own 4 KiB area at once,
+    // while group 1 is still multiplying.
     wait_vm<0>();
-    __syncthreads();
     float* wl = (float*)smem + wave * EPI_WAVE_FLOATS;
 #pragma unroll
     for (int i = 0; i < C::TM; ++i)
