@@ -184,4 +184,57 @@ __device__ __forceinline__ void epi_block(const EpiParams& p, const f32x16& acc,
     __builtin_amdgcn_wave_barrier();
 }
 
+// Gated-residual epilogue of a wave's TM x TN accumulator blocks with the
+// residual stream read ahead: the h values of block b + 2 are loaded before
+// block b is stored (distinct addresses), so the load latency overlaps the
+// work on earlier blocks instead of every block waiting for its own loads.
+// Same arithmetic as epi_block<EPI_GATED>; ragged columns fall back to it.
+template <int TM, int TN>
+__device__ __forceinline__ void epi_tile_gated(const EpiParams& p, const f32x16 (&acc)[TM][TN], float* wl, int mb0,
+                                               int nb0, int M, int N, int lane) {
+    const int c0 = (lane & 7) * 4;
+    auto fetch = [&](int b, f32x4 (&hv)[4]) {
+        const int i = b / TN, j = b % TN;
+        const int n = nb0 + j * 32 + c0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int m = mb0 + i * 32 + (lane >> 3) + 8 * q;
+            hv[q] = (m < M && n + 3 < N) ? *(const f32x4*)((const float*)p.out + (long long)m * p.ldo + n) : f32x4{};
+        }
+    };
+    constexpr int AHEAD = 2;                       // blocks whose h loads are in flight
+    f32x4 hq[AHEAD + 1][4];
+#pragma unroll
+    for (int b = 0; b < AHEAD && b < TM * TN; ++b) fetch(b, hq[b]);
+#pragma unroll
+    for (int b = 0; b < TM * TN; ++b) {
+        const int i = b / TN, j = b % TN;
+        if (b + AHEAD < TM * TN) fetch(b + AHEAD, hq[(b + AHEAD) % (AHEAD + 1)]);
+        f32x4 (&hcur)[4] = hq[b % (AHEAD + 1)];
+        const int mb = mb0 + i * 32, nb = nb0 + j * 32;
+        if (nb + 32 > N) {   // ragged columns: the per-element path
+            epi_block<EPI_GATED>(p, acc[i][j], wl, mb, nb, M, N, lane);
+        } else {
+            const int li = lane & 31, lh = lane >> 5;
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) wl[(8 * g + 4 * lh + r) * EPI_RP + li] = acc[i][j][g * 4 + r];
+            __builtin_amdgcn_wave_barrier();
+            const int n = nb + c0;
+            const f32x4 bias = p.bias ? *(const f32x4*)(p.bias + n) : f32x4{};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int row = (lane >> 3) + 8 * q;
+                const int m = mb + row;
+                if (m >= M) continue;
+                const f32x4 v = *(const f32x4*)(wl + row * EPI_RP + c0) + bias;
+                *(f32x4*)((float*)p.out + (long long)m * p.ldo + n) =
+                    hcur[q] + *(const f32x4*)(p.gate.at((long long)m) + n) * v;
+            }
+            __builtin_amdgcn_wave_barrier();
+        }
+    }
+}
+
 }  // namespace cfm

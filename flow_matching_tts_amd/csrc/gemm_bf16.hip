@@ -778,11 +778,15 @@ gemm_pp64_kernel(const bf16* __restrict__ A, int lda, const bf16* __restrict__ W
     // while group 1 is still multiplying.
     wait_vm<0>();
     float* wl = (float*)smem + wave * EPI_WAVE_FLOATS;
+    if constexpr (EPI == EPI_GATED) {
+        epi_tile_gated<C::TM, C::TN>(ep, acc, wl, m0 + grp * C::WM, n0 + wn * C::WN, M, N, lane);
+    } else {
 #pragma unroll
-    for (int i = 0; i < C::TM; ++i)
+        for (int i = 0; i < C::TM; ++i)
 #pragma unroll
-        for (int j = 0; j < C::TN; ++j)
-            epi_block<EPI>(ep, acc[i][j], wl, m0 + grp * C::WM + i * 32, n0 + wn * C::WN + j * 32, M, N, lane);
+            for (int j = 0; j < C::TN; ++j)
+                epi_block<EPI>(ep, acc[i][j], wl, m0 + grp * C::WM + i * 32, n0 + wn * C::WN + j * 32, M, N, lane);
+    }
 }
 
 template <typename C, int EPI>

@@ -202,3 +202,19 @@ def test_mask_with_holes_and_ragged_rows_matches_oracle():
     print(f"holes: rel-L2 {err:.3e}")
     assert err <= TOL[s.dtype], err
     np.testing.assert_array_equal(got[~valid], I["x0"][~valid])
+
+
+def test_masked_three_branch_speaker_batch_matches_oracle():
+    """Packed rows with the speaker branch: the per-row modulation vectors (the
+    speaker branch reads its request's own conditioning vector) are looked up
+    through the packed token -> row table."""
+    s = reduced("multicond_rf").replace(n_requests=3, n_frames=150, varlen=(20, 150))
+    W, I = synth.make_weights(s, 381), synth.make_inputs(s, 382)
+    assert I["mask"] is not None and I["spk"] is not None
+    got, _ = run_sampler(s, W, I)
+    want = O.sample(W, s, I["x0"], I["cond"], I["spk"], I["mask"], s.n_steps, s.guidance)
+    valid = _valid(I, s)
+    err = rel_l2(got, want, valid)
+    print(f"masked multicond: rel-L2 {err:.3e}")
+    assert err <= TOL[s.dtype], err
+    np.testing.assert_array_equal(got[~valid], I["x0"][~valid])
