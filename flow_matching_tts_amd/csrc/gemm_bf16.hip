@@ -5,21 +5,25 @@
 // feeds 8 consecutive k of one A row and 8 consecutive k of one W row, so LDS
 // tiles are read with 16-byte loads and never transposed.
 //
-// A block computes a BM x BN output tile with WGM x WGN waves; each wave owns a
-// (BM/WGM) x (BN/WGN) sub-tile made of 32x32 MFMA blocks. K is staged BK at a
-// time through two LDS buffers: the next stage's global loads are issued at the
-// top of an iteration and written to the other buffer at its end, and inside a
-// stage the fragments of k-step ks+1 are read from LDS while the MFMAs of
-// k-step ks run. LDS rows are padded by 16 bytes so the 16-byte fragment reads
-// of consecutive rows fall on distinct banks.
+// Kernel family (the `tile` argument selects one; 0 picks by problem size):
+//  - gemm_bf16_kernel: register-staged. A block computes a BM x BN tile with
+//    WGM x WGN waves; K is staged BK at a time through two padded LDS buffers
+//    (global loads of the next stage issued at the top of an iteration, written
+//    to the other buffer at its end; fragments of k-step ks+1 read while the
+//    MFMAs of ks run). Small problems and fp32 A operands (rounded to bf16 while
+//    staging, so no conversion pass touches HBM).
+//  - gemm_dtl_kernel / gemm_dtlp_kernel: 256x256 tiles, operands loaded straight
+//    into an LDS ring by buffer_load ... lds, all waves in lockstep.
+//  - gemm_pp_kernel / gemm_pp64_kernel: the same loads, with the 8 waves in two
+//    groups that alternate load and multiply phases (ping-pong); K stage 32 or
+//    64. gemm_pp64_kernel is the default for large problems.
+// Every variant writes its output through the same per-wave LDS-staged
+// epilogues (epilogue.h).
 //
 // Blocks are numbered so that the tiles one XCD runs at the same time share
 // operand rows in that XCD's L2: the hardware deals block ids round-robin to
 // the 8 XCDs, so each XCD's ids are mapped to a contiguous range of tile
 // numbers, and tiles are walked in groups of GROUP_M block-rows.
-//
-// fp32 A operands (latent x and condition features) are rounded to bf16 while
-// being staged, so no separate conversion pass touches HBM.
 #include <algorithm>
 #include <type_traits>
 
