@@ -180,12 +180,13 @@ cfm_status cfm_cfg_euler(const float* v, const float* w, int nb, float dt, const
  *   3: gated residual C(fp32) += gate[n] * (acc + bias[n]) with gate device fp32 [N].
  * K % 8 == 0 (bf16 A) or K % 4 == 0 (fp32 A); lda, ldw multiples of 8 (bf16)
  * or 4 (fp32 A); ldw >= K rounded up to 8 with zero padding.
- * tile: 0 = chosen from the problem size (what cfm_sample uses); 1..13 force
+ * tile: 0 = chosen from the problem size (what cfm_sample uses); 1..14 force
  * one tile configuration (1 = 128x128, 2..5 = 256x256 / 256x128 register-staged,
  * 6 = 128x128 with K stage 64, 7..9 = 256x256 direct-to-LDS, 10 = 64x64,
  * 11..12 = 256x256 direct-to-LDS with operand fragments read a stage ahead,
- * 13 = 256x256 direct-to-LDS, two wave groups alternating loads and MFMAs);
- * configurations above 1 need a bf16 A operand. The GELU of epilogue 2 is
+ * 13 = 256x256 direct-to-LDS, two wave groups alternating loads and MFMAs,
+ * 14 = as 13 with a K stage of 64); a value outside 0..14 returns
+ * CFM_E_VALUE, as does a tile above 1 with an fp32 A operand. The GELU of epilogue 2 is
  * evaluated with an erfc approximation of absolute error below 2e-7. */
 cfm_status cfm_gemm_bf16(const void* A, int a_is_f32, int lda, const void* W, int ldw,
                          const float* bias, int M, int N, int K, int epilogue,
