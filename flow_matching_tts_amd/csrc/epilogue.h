@@ -185,7 +185,7 @@ __device__ __forceinline__ void epi_block(const EpiParams& p, const f32x16& acc,
 }
 
 // Gated-residual epilogue of a wave's TM x TN accumulator blocks with the
-// residual stream read ahead: the h values of block b + 2 are loaded before
+// residual stream read ahead: the h values of block b + 5 are loaded before
 // block b is stored (distinct addresses), so the load latency overlaps the
 // work on earlier blocks instead of every block waiting for its own loads.
 // Same arithmetic as epi_block<EPI_GATED>; ragged columns fall back to it.
@@ -202,7 +202,9 @@ __device__ __forceinline__ void epi_tile_gated(const EpiParams& p, const f32x16 
             hv[q] = (m < M && n + 3 < N) ? *(const f32x4*)((const float*)p.out + (long long)m * p.ldo + n) : f32x4{};
         }
     };
-    constexpr int AHEAD = 2;                       // blocks whose h loads are in flight
+    // blocks whose h loads are in flight: 5 of a wave's 8 blocks (96 VGPRs beside the
+    // accumulators, the most that fits in 256 without spilling; 2 ahead was 2-4% slower)
+    constexpr int AHEAD = 5;
     f32x4 hq[AHEAD + 1][4];
 #pragma unroll
     for (int b = 0; b < AHEAD && b < TM * TN; ++b) fetch(b, hq[b]);
