@@ -19,7 +19,7 @@ __device__ __forceinline__ void epi_store(const EpiParams& p, int m, int n, floa
         ((ActT*)p.out)[(long long)m * p.ldo + n] = to_out<ActT>(acc + b);
     } else if constexpr (EPI == EPI_GELU_ACT) {
         // bf16 outputs: the approximation is exact to far below the output rounding
-        const float g = std::is_same<ActT, bf16>::value ? gelu_as(acc + b) : gelu_erf(acc + b);
+        const float g = std::is_same<ActT, bf16>::value ? gelu_bf16(acc + b) : gelu_erf(acc + b);
         ((ActT*)p.out)[(long long)m * p.ldo + n] = to_out<ActT>(g);
     } else if constexpr (EPI == EPI_GATED) {
         float* h = (float*)p.out + (long long)m * p.ldo + n;
@@ -67,7 +67,7 @@ __device__ __forceinline__ void epi_store_vec4(const EpiParams& p, int m, int n,
         *(f32x4*)((float*)p.out + (long long)m * p.ldo + n) = v;
     } else if constexpr (EPI == EPI_ACT || EPI == EPI_GELU_ACT || EPI == EPI_QKV) {
         if constexpr (EPI == EPI_GELU_ACT) {
-            v[0] = gelu_as(v[0]); v[1] = gelu_as(v[1]); v[2] = gelu_as(v[2]); v[3] = gelu_as(v[3]);
+            v[0] = gelu_bf16(v[0]); v[1] = gelu_bf16(v[1]); v[2] = gelu_bf16(v[2]); v[3] = gelu_bf16(v[3]);
         }
         bf16x4 b;
         b[0] = (bf16)v[0]; b[1] = (bf16)v[1]; b[2] = (bf16)v[2]; b[3] = (bf16)v[3];

@@ -187,7 +187,7 @@ cfm_status cfm_cfg_euler(const float* v, const float* w, int nb, float dt, const
  * 13 = 256x256 direct-to-LDS, two wave groups alternating loads and MFMAs,
  * 14 = as 13 with a K stage of 64); a value outside 0..14 returns
  * CFM_E_VALUE, as does a tile above 1 with an fp32 A operand. The GELU of epilogue 2 is
- * evaluated with an erfc approximation of absolute error below 2e-7. */
+ * evaluated with an erfc approximation of relative error below 1e-5 (bf16 rounding: 2^-9). */
 cfm_status cfm_gemm_bf16(const void* A, int a_is_f32, int lda, const void* W, int ldw,
                          const float* bias, int M, int N, int K, int epilogue,
                          const float* gate, void* C, int ldc, int tile, void* stream);
