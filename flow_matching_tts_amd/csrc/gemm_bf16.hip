@@ -636,13 +636,18 @@ void launch_pp(const bf16* A, int lda, const bf16* W, int ldw, int M, int N, int
 // Ping-pong with K stage 64 (tile 14): 128-byte LDS rows (one cache line per
 // row per stage, eight rows per load instruction), a 2-slot ring of 64 KiB
 // slots, and phases of 32 MFMAs, so a barrier pair is paid per 64 of K instead
-// of 32. Each wave loads 1/8 of every stage. Group 0 issues its part of stage
-// j at the start of its M(j - 1) (after the barrier that ends group 1's reads
-// of stage j - 2, same slot) and awaits it at the end of its C(j - 1); group 1
-// issues its part of stage j at the end of its M(j - 2), once its own reads of
-// stage j - 2 are complete (group 0 read that slot a phase earlier), and awaits
-// it at the end of its M(j - 1). Both waits come before the barrier after which
-// group 0 reads stage j, and both leave two phases for the loads to land.
+// of 32. A slot is refilled only when every other reader of the rows a wave
+// loads has passed a barrier after reading them. Group 0's waves load A (64 rows
+// each, read by the waves of both groups) at the start of their M(j - 1), after
+// the barrier that ends group 1's reads of stage j - 2 (same slot; group 0 read
+// it a phase earlier). Group 1's waves load W, each exactly the 64 rows of the
+// column quarter it multiplies, at the end of their M(j - 2), right after their
+// own reads of the slot: the only other reader of those rows, the group-0 wave
+// of the same quarter, read them a phase earlier. (A split in which every wave
+// loads rows that other waves of its own group read would race here.) Group 0
+// awaits its part at the end of its C(j - 1), group 1 at the end of its M(j - 1):
+// both waits come before the barrier after which group 0 reads stage j, and both
+// leave two phases for the loads to land.
 constexpr int BK64 = 64;
 
 __device__ __forceinline__ int swz64(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
@@ -696,8 +701,10 @@ gemm_pp64_kernel(const bf16* __restrict__ A, int lda, const bf16* __restrict__ W
                  int M, int N, int K, int tm, int tn, EpiParams ep) {
     static_assert(C::WGM == 2 && C::WGN == 4, "two groups of four waves");
     constexpr int SLOT = (C::BM + C::BN) * BK64;                // bf16 elements
-    constexpr int AI = C::BM / 8 / C::NW, WI = C::BN / 8 / C::NW;   // loads per wave per stage
-    constexpr int L = AI + WI;
+    // group 0's waves load A (64 rows each), group 1's waves W (each the 64 rows of
+    // the column quarter it multiplies): L loads of 8 rows per wave per stage
+    static_assert(C::BM == C::BN && C::BM % (8 * C::WGN) == 0, "equal shares");
+    constexpr int L = C::BM / 8 / C::WGN;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     bf16* const ring = (bf16*)smem;
     const unsigned ring_addr = (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)smem;
@@ -724,10 +731,10 @@ gemm_pp64_kernel(const bf16* __restrict__ A, int lda, const bf16* __restrict__ W
 #pragma unroll
         for (int j = 0; j < C::TN; ++j) acc[i][j] = f32x16{};
 
-    auto issue = [&](int stage) {   // this wave's 1/8 of the stage's rows
+    auto issue = [&](int stage) {   // this wave's share of the stage's rows
         const unsigned slot = ring_addr + (unsigned)((stage & 1) * SLOT * 2);
-        dma_stage64<AI>(ra, lda, M, K, m0, stage * BK64, slot, wave, lane);
-        dma_stage64<WI>(rw, ldw, N, K, n0, stage * BK64, slot + C::BM * BK64 * 2, wave, lane);
+        if (grp == 0) dma_stage64<L>(ra, lda, M, K, m0, stage * BK64, slot, wn, lane);
+        else dma_stage64<L>(rw, ldw, N, K, n0, stage * BK64, slot + C::BM * BK64 * 2, wn, lane);
     };
     auto sync = [&] {
         __builtin_amdgcn_sched_barrier(0);
@@ -765,7 +772,11 @@ gemm_pp64_kernel(const bf16* __restrict__ A, int lda, const bf16* __restrict__ W
     } else {
         for (int k = 0; k < nk; ++k) {
             if (k == 0) sync();
-            reads(k);                       // complete before the slot is refilled below
+            // stage k + 2 reuses the slot of stage k. This wave refills only the W
+            // rows it multiplies itself (reads complete just above); their only
+            // other reader, the group-0 wave of the same column quarter, read
+            // them a phase earlier, before the last barrier.
+            reads(k);
             if (k + 2 < nk) issue(k + 2);
             if (k + 1 < nk) {               // this wave's part of stage k + 1 has landed
                 if (k + 2 < nk) wait_vm<L>();

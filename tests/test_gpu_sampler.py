@@ -88,7 +88,11 @@ def test_full_workload_matches_stored_oracle(name):
     s = synth.workload(name)
     z = _golden(name)
     W, I = synth.make_weights(s), synth.make_inputs(s)
-    got, _ = run_sampler(s, W, I)
+    got, smp = run_sampler(s, W, I)
+    # repeat determinism at full size in the bench's launch configuration: a second call
+    # on the same context gives the same bits (every kernel's reduction order is fixed)
+    again, _ = run_sampler(s, W, I, sampler=smp)
+    np.testing.assert_array_equal(again, got)
     reqs, frames = z["requests"], z["frames"]
     g = got[reqs][:, frames, :]
     valid = _valid(I, s)[reqs][:, frames]
