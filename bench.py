@@ -16,6 +16,7 @@ Prints ONE JSON line on stdout:
                    HBM-side bytes per launch from the committed rocprofv3 counter summary
                    (profiles/traffic_mel_dit.txt), null once the GEMM sources differ
   cpu_baseline     the fp64 CPU oracle on a bounded sample of the same workload
+  cfg_euler_cold   the CFG + Euler kernel alone with the last-level cache flushed before each launch
 """
 from __future__ import annotations
 
@@ -64,6 +65,34 @@ def work_model(s, lengths):
         "cfg_euler": (x_v * C * 4 * (2 + nb), S),
     }
     return w
+
+
+def cfg_euler_cold(s, reps: int = 20):
+    """The CFG + Euler kernel alone on the workload's shapes with the 256 MiB last-level cache flushed
+    (a 512 MiB device write) before every launch: per-launch time (HIP events around the launch on the
+    current stream) and algorithmic bytes over it. The in-pipeline figure is in kernels["cfg_euler"]."""
+    import torch
+    import flow_matching_tts_amd as F
+    R, Tx, C, nb = s.n_requests, s.n_frames, s.latent_dim, s.n_branches
+    g = torch.Generator(device="cuda").manual_seed(7)
+    v = torch.randn(nb, R, Tx, C, device="cuda", generator=g)
+    x = torch.randn(R, Tx, C, device="cuda", generator=g)
+    w = [1.0] if nb == 1 else ([1 - s.guidance[0], s.guidance[0]] if nb == 2 else
+                               [1 - s.guidance[0], s.guidance[0] - s.guidance[1], s.guidance[1]])
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for i in range(reps):
+        scratch.fill_(i & 0xFF)
+        ev[i][0].record()
+        F.cfg_euler(v, w, 1.0 / s.n_steps, x)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    us = float(np.median([a.elapsed_time(b) * 1e3 for a, b in ev]))
+    nbytes = R * Tx * C * 4 * (2 + nb)
+    del scratch
+    return {"bytes": nbytes, "mean_us": us, "rate": nbytes / us / 1e3, "rate_unit": "GB/s",
+            "frac": nbytes / (us * 1e-6) / PEAK_HBM, "flush": "512 MiB device write before each launch",
+            "reps": reps}
 
 
 def cpu_baseline(s, W, I, max_workers: int):
@@ -237,6 +266,7 @@ def main():
     else:
         roofline, gemm_attn_frac = None, None
         mf = sum(model[c][0] * model[c][1] for c in MFMA_CLASSES)
+    k1_cold = None if args.no_kernel_timing or s.dtype != "bf16" else cfg_euler_cold(s)
 
     res = {
         "metric": "estimator evals/sec and latent frames/sec per step; % bf16 MFMA peak",
@@ -257,6 +287,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": base,
         "kernels": kernels,
+        "cfg_euler_cold": k1_cold,
     }
     print(json.dumps(res), flush=True)
 
