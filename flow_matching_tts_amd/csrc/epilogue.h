@@ -61,8 +61,10 @@ __device__ __forceinline__ void epi_store(const EpiParams& p, int m, int n, floa
 // Vector epilogue of 4 consecutive columns n..n+3 of one row m (in range, 16-byte
 // aligned). Same arithmetic as epi_store, one wide access per operand.
 template <int EPI>
-__device__ __forceinline__ void epi_store_vec4(const EpiParams& p, int m, int n, f32x4 v) {
-    if (p.bias) v += *(const f32x4*)(p.bias + n);
+__device__ __forceinline__ void epi_store_vec4(const EpiParams& p, int m, int n, f32x4 v,
+                                               const f32x4* bias4 = nullptr) {
+    if (bias4) v += *bias4;                        // preloaded by the caller (same columns)
+    else if (p.bias) v += *(const f32x4*)(p.bias + n);
     if constexpr (EPI == EPI_F32) {
         *(f32x4*)((float*)p.out + (long long)m * p.ldo + n) = v;
     } else if constexpr (EPI == EPI_ACT || EPI == EPI_GELU_ACT || EPI == EPI_QKV) {
@@ -113,9 +115,16 @@ __device__ __forceinline__ void epi_store_vec4(const EpiParams& p, int m, int n,
 constexpr int EPI_RP = 32;
 constexpr int EPI_WAVE_FLOATS = 32 * EPI_RP;
 
-template <int EPI>
+// bias4 / bias1, when given, hold the bias of this lane's columns (nb0 + 4 (lane % 8)
+// .. + 3; nb0 + lane % 32 for the transposed V columns), loaded by the caller before
+// any store: a global load placed after stores waits for those stores as well (one
+// vmcnt counter for both), which serialises an epilogue on store completion. PK =
+// false drops the packed-row lookups (tok_row must then be null), so that path
+// issues no load at all.
+template <int EPI, bool PK = true>
 __device__ __forceinline__ void epi_block(const EpiParams& p, const f32x16& acc, float* wl, int mb, int nb0,
-                                          int M, int N, int lane) {
+                                          int M, int N, int lane, const f32x4* bias4 = nullptr,
+                                          const float* bias1 = nullptr) {
     const int li = lane & 31, lh = lane >> 5;
 #pragma unroll
     for (int g = 0; g < 4; ++g)
@@ -127,7 +136,7 @@ __device__ __forceinline__ void epi_block(const EpiParams& p, const f32x16& acc,
             // lane: column li, rows 16 lh .. 16 lh + 15 (consecutive sequence positions)
             const int n = nb0 + li;
             if (n < N) {
-                const float b = p.bias ? p.bias[n] : 0.0f;
+                const float b = bias1 ? *bias1 : p.bias ? p.bias[n] : 0.0f;
                 const int c = n - p.d2, hh = c >> 6, e = c & 63;
 #pragma unroll
                 for (int q8 = 0; q8 < 2; ++q8) {
@@ -136,15 +145,16 @@ __device__ __forceinline__ void epi_block(const EpiParams& p, const f32x16& acc,
 #pragma unroll
                     for (int r = 0; r < 8; ++r) vals[r] = wl[(r0 + r) * EPI_RP + li] + b;
                     if (m >= M) continue;
-                    const int row = p.tok_row ? p.tok_row[m] : m / p.T;
-                    const int t = m - (p.tok_row ? p.row_off[row] : row * p.T);
-                    const int len = p.tok_row ? p.row_off[row + 1] - p.row_off[row] : p.T;
+                    const bool pk = PK && p.tok_row != nullptr;
+                    const int row = pk ? p.tok_row[m] : m / p.T;
+                    const int t = m - (pk ? p.row_off[row] : row * p.T);
+                    const int len = pk ? p.row_off[row + 1] - p.row_off[row] : p.T;
                     if (m + 7 < M && t + 7 < len && (t & 7) == 0) {
                         bf16x8 o;
 #pragma unroll
                         for (int r = 0; r < 8; ++r) o[r] = (bf16)vals[r];
                         *(bf16x8*)(p.vt + ((long long)(row * p.H + hh) * 64 + e) * p.Tp + t) = o;
-                    } else if (p.tok_row) {   // rare (row boundaries): rolled, reads LDS again
+                    } else if (pk) {   // rare (row boundaries): rolled, reads LDS again
 #pragma unroll 1
                         for (int r = 0; r < 8 && m + r < M; ++r) {
                             const int rw = p.tok_row[m + r], tt = (m + r) - p.row_off[rw];
@@ -174,7 +184,7 @@ __device__ __forceinline__ void epi_block(const EpiParams& p, const f32x16& acc,
         const int m = mb + row, n = nb0 + c0;
         if (m >= M) continue;
         if (n + 3 < N) {
-            epi_store_vec4<EPI>(p, m, n, v);
+            epi_store_vec4<EPI>(p, m, n, v, bias4);
         } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
@@ -185,57 +195,64 @@ __device__ __forceinline__ void epi_block(const EpiParams& p, const f32x16& acc,
 }
 
 // Gated-residual epilogue of a wave's TM x TN accumulator blocks with the
-// residual stream read ahead: the h values of block b + 5 are loaded before
-// block b is stored (distinct addresses), so the load latency overlaps the
-// work on earlier blocks instead of every block waiting for its own loads.
-// Same arithmetic as epi_block<EPI_GATED>; ragged columns fall back to it.
+// residual stream and the gate read ahead: the h and gate values of block b +
+// AHEAD are loaded before block b is stored (distinct addresses), and the bias of
+// every column before the first store, so no load result is waited for behind
+// stores (one vmcnt counter covers both). Tiles with ragged columns take the
+// per-element path of epi_block. Same arithmetic as epi_block<EPI_GATED>.
 template <int TM, int TN>
 __device__ __forceinline__ void epi_tile_gated(const EpiParams& p, const f32x16 (&acc)[TM][TN], float* wl, int mb0,
                                                int nb0, int M, int N, int lane) {
+    if (nb0 + TN * 32 > N) {   // ragged columns somewhere in this wave's tile
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) epi_block<EPI_GATED>(p, acc[i][j], wl, mb0 + i * 32, nb0 + j * 32, M, N, lane);
+        return;
+    }
     const int c0 = (lane & 7) * 4;
-    auto fetch = [&](int b, f32x4 (&hv)[4]) {
+    f32x4 bias[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) bias[j] = p.bias ? *(const f32x4*)(p.bias + nb0 + j * 32 + c0) : f32x4{};
+    auto fetch = [&](int b, f32x4 (&hv)[4], f32x4 (&gv)[4]) {
         const int i = b / TN, j = b % TN;
         const int n = nb0 + j * 32 + c0;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int m = mb0 + i * 32 + (lane >> 3) + 8 * q;
-            hv[q] = (m < M && n + 3 < N) ? *(const f32x4*)((const float*)p.out + (long long)m * p.ldo + n) : f32x4{};
+            const bool ok = m < M;
+            hv[q] = ok ? *(const f32x4*)((const float*)p.out + (long long)m * p.ldo + n) : f32x4{};
+            gv[q] = ok ? *(const f32x4*)(p.gate.at((long long)m) + n) : f32x4{};
         }
     };
-    // blocks whose h loads are in flight: 5 of a wave's 8 blocks (96 VGPRs beside the
-    // accumulators, the most that fits in 256 without spilling; 2 ahead was 2-4% slower)
-    constexpr int AHEAD = 5;
-    f32x4 hq[AHEAD + 1][4];
+    // blocks whose h and gate loads are in flight: one (2 x 16 VGPRs per block;
+    // two spill beside the 128 accumulator VGPRs)
+    constexpr int AHEAD = 1;
+    f32x4 hq[AHEAD + 1][4], gq[AHEAD + 1][4];
 #pragma unroll
-    for (int b = 0; b < AHEAD && b < TM * TN; ++b) fetch(b, hq[b]);
+    for (int b = 0; b < AHEAD && b < TM * TN; ++b) fetch(b, hq[b], gq[b]);
 #pragma unroll
     for (int b = 0; b < TM * TN; ++b) {
         const int i = b / TN, j = b % TN;
-        if (b + AHEAD < TM * TN) fetch(b + AHEAD, hq[(b + AHEAD) % (AHEAD + 1)]);
-        f32x4 (&hcur)[4] = hq[b % (AHEAD + 1)];
-        const int mb = mb0 + i * 32, nb = nb0 + j * 32;
-        if (nb + 32 > N) {   // ragged columns: the per-element path
-            epi_block<EPI_GATED>(p, acc[i][j], wl, mb, nb, M, N, lane);
-        } else {
-            const int li = lane & 31, lh = lane >> 5;
+        if (b + AHEAD < TM * TN) fetch(b + AHEAD, hq[(b + AHEAD) % (AHEAD + 1)], gq[(b + AHEAD) % (AHEAD + 1)]);
+        const f32x4 (&hcur)[4] = hq[b % (AHEAD + 1)];
+        const f32x4 (&gcur)[4] = gq[b % (AHEAD + 1)];
+        const int mb = mb0 + i * 32, n = nb0 + j * 32 + c0;
+        const int li = lane & 31, lh = lane >> 5;
 #pragma unroll
-            for (int g = 0; g < 4; ++g)
+        for (int g = 0; g < 4; ++g)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) wl[(8 * g + 4 * lh + r) * EPI_RP + li] = acc[i][j][g * 4 + r];
-            __builtin_amdgcn_wave_barrier();
-            const int n = nb + c0;
-            const f32x4 bias = p.bias ? *(const f32x4*)(p.bias + n) : f32x4{};
+            for (int r = 0; r < 4; ++r) wl[(8 * g + 4 * lh + r) * EPI_RP + li] = acc[i][j][g * 4 + r];
+        __builtin_amdgcn_wave_barrier();
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int row = (lane >> 3) + 8 * q;
-                const int m = mb + row;
-                if (m >= M) continue;
-                const f32x4 v = *(const f32x4*)(wl + row * EPI_RP + c0) + bias;
-                *(f32x4*)((float*)p.out + (long long)m * p.ldo + n) =
-                    hcur[q] + *(const f32x4*)(p.gate.at((long long)m) + n) * v;
-            }
-            __builtin_amdgcn_wave_barrier();
+        for (int q = 0; q < 4; ++q) {
+            const int row = (lane >> 3) + 8 * q;
+            const int m = mb + row;
+            if (m >= M) continue;
+            const f32x4 v = *(const f32x4*)(wl + row * EPI_RP + c0) + bias[j];
+            *(f32x4*)((float*)p.out + (long long)m * p.ldo + n) = hcur[q] + gcur[q] * v;
         }
+        __builtin_amdgcn_wave_barrier();
     }
 }
 

@@ -795,6 +795,31 @@ gemm_pp64_kernel(const bf16* __restrict__ A, int lda, const bf16* __restrict__ W
     float* wl = (float*)smem + wave * EPI_WAVE_FLOATS;
     if constexpr (EPI == EPI_GATED) {
         epi_tile_gated<C::TM, C::TN>(ep, acc, wl, m0 + grp * C::WM, n0 + wn * C::WN, M, N, lane);
+    } else if constexpr (EPI == EPI_F32 || EPI == EPI_ACT || EPI == EPI_GELU_ACT || EPI == EPI_QKV) {
+        // the bias of every column this lane stores, loaded before the first store
+        f32x4 b4[C::TN];
+        float b1[C::TN];
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j) {
+            const int nj = n0 + wn * C::WN + j * 32;
+            const int n4 = nj + (lane & 7) * 4, n1 = nj + li;
+            b4[j] = ep.bias && n4 + 3 < N ? *(const f32x4*)(ep.bias + n4) : f32x4{};
+            b1[j] = ep.bias && n1 < N ? ep.bias[n1] : 0.0f;
+        }
+        // one wait the compiler sees: from here on no load is outstanding, so no
+        // store below is followed by a wait for it (the counter covers stores too)
+        __builtin_amdgcn_s_waitcnt(0);
+        auto blocks = [&](auto pk) {
+#pragma unroll
+            for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+                for (int j = 0; j < C::TN; ++j)
+                    epi_block<EPI, decltype(pk)::value>(ep, acc[i][j], wl, m0 + grp * C::WM + i * 32,
+                                                        n0 + wn * C::WN + j * 32, M, N, lane, &b4[j], &b1[j]);
+        };
+        // packed rows (their lookups load) and plain rows (no load) as separate code
+        if (EPI == EPI_QKV && ep.tok_row != nullptr) blocks(std::true_type{});
+        else blocks(std::false_type{});
     } else {
 #pragma unroll
         for (int i = 0; i < C::TM; ++i)
