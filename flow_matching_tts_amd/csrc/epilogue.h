@@ -177,6 +177,34 @@ __device__ __forceinline__ void epi_block(const EpiParams& p, const f32x16& acc,
     }
     // lane: row (lane / 8) + 8 q, columns 4 (lane % 8) .. +3
     const int c0 = (lane & 7) * 4;
+    if constexpr (EPI == EPI_INPROJ) {
+        // the in-projection reads the condition term of each row: load all four rows'
+        // operands first, then store (a load after a store waits for the store too)
+        const int n = nb0 + c0;
+        if (n + 3 < N && p.row_off == nullptr) {
+            const f32x4 b = p.bias ? *(const f32x4*)(p.bias + n) : f32x4{};
+            f32x4 v[4], vc[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int m = min(mb + (lane >> 3) + 8 * q, M - 1);
+                v[q] = *(const f32x4*)(wl + ((lane >> 3) + 8 * q) * EPI_RP + c0);
+                vc[q] = p.cproj ? v[q] + *(const f32x4*)(p.cproj + (long long)m * p.ldo + n) : v[q] + b;
+                v[q] += b;
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int m = mb + (lane >> 3) + 8 * q;
+                if (m >= M) continue;
+                const int r = m / p.Tx, t = m - r * p.Tx;
+                for (int br = 0; br < p.nb; ++br) {
+                    const long long tok = (long long)(br * p.R + r) * p.T + p.P + t;
+                    *(f32x4*)((float*)p.out + tok * p.ldo + n) = br >= p.cond_branch0 ? vc[q] : v[q];
+                }
+            }
+            __builtin_amdgcn_wave_barrier();
+            return;
+        }
+    }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int row = (lane >> 3) + 8 * q;
