@@ -83,15 +83,9 @@ adaln_kernel(LnParams p, int tpw) {
     for (int it = 0; it < tpw; ++it) {
         const long long o = o0 + it;
         if (o >= p.n_out) break;
-        const bool more = it + 1 < tpw && o + 1 < p.n_out;
-        if (more) {
-            const f32x4* src = src_of(o + 1);
-#pragma unroll
-            for (int i = 0; i < V; ++i) {
-                const int c = lane + i * 64;
-                nxt[i] = c < d4 ? src[c] : f32x4{};
-            }
-        }
+        // modulation vectors first, the next token's row after them: the output
+        // below waits only for the vectors (loads complete in issue order), so its
+        // stores go out while the next row is still in flight
         const float* shp = p.shift.at(o);
         if (shp != sh_ptr) {              // wave-uniform
             sh_ptr = shp;
@@ -102,6 +96,15 @@ adaln_kernel(LnParams p, int tpw) {
                 const int c = lane + i * 64;
                 sh[i] = c < d4 ? s4[c] : f32x4{};
                 sc[i] = c < d4 ? c4[c] + 1.0f : f32x4{};
+            }
+        }
+        const bool more = it + 1 < tpw && o + 1 < p.n_out;
+        if (more) {
+            const f32x4* src = src_of(o + 1);
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+                const int c = lane + i * 64;
+                nxt[i] = c < d4 ? src[c] : f32x4{};
             }
         }
         float sum = 0.0f;
