@@ -242,6 +242,49 @@ __device__ __forceinline__ void epi_tile_gated(const EpiParams& p, const f32x16 
     f32x4 bias[TN];
 #pragma unroll
     for (int j = 0; j < TN; ++j) bias[j] = p.bias ? *(const f32x4*)(p.bias + nb0 + j * 32 + c0) : f32x4{};
+    if (p.gate.spk_branch < 0) {
+        // every row reads the same gate vector: preload it per column like the bias
+        // and read only the residual ahead, four blocks deep (64 VGPRs)
+        f32x4 gate[TN];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) gate[j] = *(const f32x4*)(p.gate.base + nb0 + j * 32 + c0);
+        constexpr int AH = 4;
+        f32x4 hq[AH + 1][4];
+        auto fetch_h = [&](int b, f32x4 (&hv)[4]) {
+            const int i = b / TN, j = b % TN;
+            const int n = nb0 + j * 32 + c0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int m = mb0 + i * 32 + (lane >> 3) + 8 * q;
+                hv[q] = m < M ? *(const f32x4*)((const float*)p.out + (long long)m * p.ldo + n) : f32x4{};
+            }
+        };
+#pragma unroll
+        for (int b = 0; b < AH && b < TM * TN; ++b) fetch_h(b, hq[b]);
+#pragma unroll
+        for (int b = 0; b < TM * TN; ++b) {
+            const int i = b / TN, j = b % TN;
+            if (b + AH < TM * TN) fetch_h(b + AH, hq[(b + AH) % (AH + 1)]);
+            const f32x4 (&hcur)[4] = hq[b % (AH + 1)];
+            const int mb = mb0 + i * 32, n = nb0 + j * 32 + c0;
+            const int li = lane & 31, lh = lane >> 5;
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) wl[(8 * g + 4 * lh + r) * EPI_RP + li] = acc[i][j][g * 4 + r];
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int row = (lane >> 3) + 8 * q;
+                const int m = mb + row;
+                if (m >= M) continue;
+                const f32x4 v = *(const f32x4*)(wl + row * EPI_RP + c0) + bias[j];
+                *(f32x4*)((float*)p.out + (long long)m * p.ldo + n) = hcur[q] + gate[j] * v;
+            }
+            __builtin_amdgcn_wave_barrier();
+        }
+        return;
+    }
     auto fetch = [&](int b, f32x4 (&hv)[4], f32x4 (&gv)[4]) {
         const int i = b / TN, j = b % TN;
         const int n = nb0 + j * 32 + c0;
