@@ -188,10 +188,8 @@ def main():
 
     import torch
     import flow_matching_tts_amd as F
-    from tests.helpers import config_for
-
     torch.cuda.set_device(0)
-    smp = F.Sampler(config_for(s), W)
+    smp = F.Sampler(F.config_from_shape(s), W)
     x0 = torch.from_numpy(I["x0"]).cuda()
     cond = torch.from_numpy(I["cond"]).cuda()
     spk = None if I["spk"] is None else torch.from_numpy(I["spk"]).cuda()

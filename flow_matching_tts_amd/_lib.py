@@ -110,6 +110,21 @@ def make_config(*, n_layers, d_model, n_heads, ffn_dim, latent_dim, cond_dim, co
                       spk_dim, t_freq_dim, n_branches, dt, max_requests, max_frames, max_steps)
 
 
+def config_from_shape(s, *, max_requests: Optional[int] = None, max_frames: Optional[int] = None,
+                      max_steps: Optional[int] = None) -> cfm_config:
+    """cfm_config of a workload description: any object with the model attributes
+    (n_layers, d_model, n_heads, ffn_dim, latent_dim, cond_dim, cond_mode, n_prefix,
+    spk_dim, n_branches, dtype, t_freq_dim) and its n_requests / n_frames / n_steps,
+    which give the capacity unless overridden."""
+    return make_config(
+        n_layers=s.n_layers, d_model=s.d_model, n_heads=s.n_heads, ffn_dim=s.ffn_dim,
+        latent_dim=s.latent_dim, cond_dim=s.cond_dim, cond_mode=s.cond_mode, n_prefix=s.n_prefix,
+        spk_dim=s.spk_dim, n_branches=s.n_branches, dtype=s.dtype, t_freq_dim=s.t_freq_dim,
+        max_requests=s.n_requests if max_requests is None else max_requests,
+        max_frames=s.n_frames if max_frames is None else max_frames,
+        max_steps=s.n_steps if max_steps is None else max_steps)
+
+
 def weights_bytes(cfg: cfm_config) -> int:
     return int(load().cfm_weights_bytes(C.byref(cfg)))
 
@@ -155,6 +170,69 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
+def _shape(t):
+    return tuple(int(v) for v in t.shape)
+
+
+def _need(name, t, shape, dtype, optional=False):
+    """Shape, dtype and layout of one tensor argument (ValueError before any launch).
+
+    ``shape`` entries that are None are not checked. Device placement is checked
+    separately, after every shape, so that a wrong shape is reported as such."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if len(t.shape) != len(shape) or any(w is not None and g != w for g, w in zip(_shape(t), shape)):
+        raise ValueError(f"{name} has shape {_shape(t)}, expected {tuple('*' if w is None else w for w in shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _on_device(**tensors):
+    devs = {n: t.device for n, t in tensors.items() if t is not None}
+    for n, d in devs.items():
+        if d.type != "cuda":
+            raise ValueError(f"{n} must be a CUDA tensor (got {d})")
+    if len(set(devs.values())) > 1:
+        raise ValueError(f"tensors on different devices: {devs}")
+
+
+def check_sample_args(cfg: cfm_config, x0, cond, mask=None, spk=None, out=None, n_steps: int = 0,
+                      guidance: Sequence[float] = ()):
+    """Validates every argument of Sampler.sample against the context's config.
+
+    cfm_sample receives bare pointers and only R, Tx and S: a tensor smaller than
+    those imply would be read or written past its end on the device, so every
+    shape is checked here first."""
+    import torch
+    if len(x0.shape) != 3:
+        raise ValueError(f"x0 must be [R, Tx, latent_dim], got shape {_shape(x0)}")
+    R, Tx = int(x0.shape[0]), int(x0.shape[1])
+    _need("x0", x0, (R, Tx, cfg.latent_dim), torch.float32)
+    if cfg.cond_mode == CFM_COND_PREFIX:
+        _need("cond", cond, (R, cfg.n_prefix, cfg.latent_dim), torch.float32)
+    else:
+        _need("cond", cond, (R, Tx, cfg.cond_dim), torch.float32)
+    _need("mask", mask, (R, Tx), torch.uint8, optional=True)
+    if cfg.spk_dim > 0:
+        _need("spk", spk, (R, cfg.spk_dim), torch.float32)
+    elif spk is not None:
+        raise ValueError("spk given, but the config has no speaker path (spk_dim == 0)")
+    _need("out", out, (R, Tx, cfg.latent_dim), torch.float32, optional=True)
+    if len(guidance) != cfg.n_branches - 1:
+        raise ValueError(f"{cfg.n_branches} branches take {cfg.n_branches - 1} guidance scales, "
+                         f"got {len(guidance)}")
+    if int(n_steps) < 0:
+        raise ValueError("n_steps must be >= 0")
+    if R > cfg.max_requests or Tx > cfg.max_frames or int(n_steps) > cfg.max_steps:
+        raise ValueError(f"R={R} Tx={Tx} S={n_steps} above the capacity "
+                         f"{cfg.max_requests}/{cfg.max_frames}/{cfg.max_steps}")
+    _on_device(x0=x0, cond=cond, mask=mask, spk=spk, out=out)
+
+
 def _stream(stream) -> Optional[int]:
     import torch
     s = torch.cuda.current_stream() if stream is None else stream
@@ -195,12 +273,11 @@ class Sampler:
                out=None, stream=None):
         """out[R, Tx, C] (fp32, device) after n_steps Euler steps; out may be x0 itself."""
         import torch
+        guidance = tuple(guidance)
+        check_sample_args(self.cfg, x0, cond, mask, spk, out, n_steps, guidance)
+        if x0.device != self.weights.device:
+            raise ValueError(f"inputs on {x0.device}, sampler on {self.weights.device}")
         R, Tx = int(x0.shape[0]), int(x0.shape[1])
-        for name, t, dt in (("x0", x0, torch.float32), ("cond", cond, torch.float32),
-                            ("spk", spk, torch.float32), ("mask", mask, torch.uint8),
-                            ("out", out, torch.float32)):
-            if t is not None and (t.dtype != dt or not t.is_contiguous() or not t.is_cuda):
-                raise ValueError(f"{name} must be a contiguous CUDA {dt} tensor")
         if out is None:
             out = torch.empty_like(x0)
         g = (C.c_float * max(1, len(guidance)))(*[float(v) for v in guidance])
@@ -223,7 +300,17 @@ class Sampler:
 # ---------------------------------------------------------------- single kernels
 
 def cfg_euler(v, w: Sequence[float], dt: float, x, mask=None, stream=None):
-    nb, R, Tx, Cc = (int(s) for s in v.shape)
+    """x[r, t] += dt * sum_b w[b] v[b, r, t] on valid frames; v [nb, R, Tx, C], x [R, Tx, C] fp32."""
+    import torch
+    if len(v.shape) != 4:
+        raise ValueError(f"v must be [nb, R, Tx, C], got shape {_shape(v)}")
+    nb, R, Tx, Cc = _shape(v)
+    _need("v", v, (nb, R, Tx, Cc), torch.float32)
+    _need("x", x, (R, Tx, Cc), torch.float32)
+    _need("mask", mask, (R, Tx), torch.uint8, optional=True)
+    if len(w) != nb:
+        raise ValueError(f"{nb} branches take {nb} weights, got {len(w)}")
+    _on_device(v=v, x=x, mask=mask)
     ww = (C.c_float * nb)(*[float(a) for a in w])
     check(load().cfm_cfg_euler(_ptr(v), ww, nb, float(dt), _ptr(mask), R, Tx, Cc, _ptr(x), _stream(stream)))
     return x
@@ -231,31 +318,67 @@ def cfg_euler(v, w: Sequence[float], dt: float, x, mask=None, stream=None):
 
 def gemm_bf16(A, W, bias=None, *, epilogue: int, out, gate=None, K: Optional[int] = None, tile: int = 0,
               stream=None):
-    """out = epilogue(A[:, :K] W[:, :K]^T + bias); A bf16 or fp32, W bf16 [N, ldw]."""
+    """out = epilogue(A[:, :K] W[:, :K]^T + bias); A bf16 or fp32 [M, lda], W bf16 [N, ldw]."""
     import torch
-    M, lda = int(A.shape[0]), int(A.shape[1])
-    N, ldw = int(W.shape[0]), int(W.shape[1])
+    if len(A.shape) != 2 or len(W.shape) != 2 or len(out.shape) != 2:
+        raise ValueError("A, W and out must be 2-D")
+    M, lda = _shape(A)
+    N, ldw = _shape(W)
     K = lda if K is None else int(K)
+    if not 0 <= K <= lda:
+        raise ValueError(f"K={K} outside [0, lda={lda}]")
+    if A.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError(f"A must be bf16 or fp32, got {A.dtype}")
+    _need("A", A, (M, lda), A.dtype)
+    _need("W", W, (N, ldw), torch.bfloat16)
+    _need("bias", bias, (N,), torch.float32, optional=True)
+    out_dtype = torch.bfloat16 if epilogue in (1, 2) else torch.float32
+    _need("out", out, (M, None), out_dtype)
+    if int(out.shape[1]) < N:
+        raise ValueError(f"out has {int(out.shape[1])} columns, needs at least N={N}")
+    if epilogue == 3:
+        _need("gate", gate, (N,), torch.float32)
     a_f32 = 1 if A.dtype == torch.float32 else 0
+    _on_device(A=A, W=W, bias=bias, out=out, gate=gate)
     check(load().cfm_gemm_bf16(_ptr(A), a_f32, lda, _ptr(W), ldw, _ptr(bias), M, N, K, int(epilogue),
                                _ptr(gate), _ptr(out), int(out.shape[1]), int(tile), _stream(stream)))
     return out
 
 
 def attention_bf16(qk, vt, kv_len, o, *, n_heads: int, key_mask=None, stream=None):
-    """qk bf16 [rows, T, 2*H*64], vt bf16 [rows, H, 64, Tp] (Tp = T rounded up to 64)."""
+    """qk bf16 [rows, T, 2*H*64], vt bf16 [rows, H, 64, Tp] (Tp = T rounded up to 64),
+    kv_len int32 [rows], key_mask uint8 [rows, T] or None, o bf16 [rows, T, H*64]."""
     import torch
+    H = int(n_heads)
+    if len(qk.shape) != 3:
+        raise ValueError(f"qk must be [rows, T, 2*H*64], got shape {_shape(qk)}")
     rows, T = int(qk.shape[0]), int(qk.shape[1])
     Tp = (T + 63) // 64 * 64
+    _need("qk", qk, (rows, T, 2 * H * 64), torch.bfloat16)
+    _need("vt", vt, (rows, H, 64, Tp), torch.bfloat16)
+    _need("kv_len", kv_len, (rows,), torch.int32)
+    _need("key_mask", key_mask, (rows, T), torch.uint8, optional=True)
+    _need("o", o, (rows, T, H * 64), torch.bfloat16)
+    _on_device(qk=qk, vt=vt, kv_len=kv_len, key_mask=key_mask, o=o)
     scratch = torch.empty(rows * 4 + rows * Tp + rows * (Tp // 64) + 64, dtype=torch.uint8, device=qk.device)
     check(load().cfm_attention_bf16(_ptr(qk), _ptr(vt), _ptr(kv_len), _ptr(key_mask), rows, T,
-                                    int(n_heads), _ptr(scratch), scratch.numel(), _ptr(o), _stream(stream)))
+                                    H, _ptr(scratch), scratch.numel(), _ptr(o), _stream(stream)))
     return o
 
 
 def adaln(h, shift, scale, y, stream=None):
+    """y = LN(h) * (1 + scale) + shift; h fp32 [M, d], shift / scale fp32 [d], y fp32 or bf16 [M, d]."""
     import torch
-    M, d = int(h.shape[0]), int(h.shape[1])
+    if len(h.shape) != 2:
+        raise ValueError(f"h must be [M, d], got shape {_shape(h)}")
+    M, d = _shape(h)
+    _need("h", h, (M, d), torch.float32)
+    _need("shift", shift, (d,), torch.float32)
+    _need("scale", scale, (d,), torch.float32)
+    if y.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError(f"y must be fp32 or bf16, got {y.dtype}")
+    _need("y", y, (M, d), y.dtype)
+    _on_device(h=h, shift=shift, scale=scale, y=y)
     check(load().cfm_adaln(_ptr(h), _ptr(shift), _ptr(scale), M, d, 1 if y.dtype == torch.bfloat16 else 0,
                            _ptr(y), _stream(stream)))
     return y

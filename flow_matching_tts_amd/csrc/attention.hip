@@ -586,6 +586,12 @@ void launch_attn_nw(const AttnParams& p, hipStream_t s) {
     attn_bf16_kernel<NW><<<grid, 64 * NW, attn_lds_bytes<NW>(p.Tp), s>>>(p);
 }
 
+bool attention_bf16_fits(long long T) {
+    if (T <= 64) return true;   // one key tile: the short kernel, static LDS
+    const long long Tp = (T + 63) / 64 * 64;
+    return Tp <= (1LL << 30) && attn_lds_bytes<8>((int)Tp) <= 160 * 1024;
+}
+
 void launch_attention_bf16(const AttnParams& p, hipStream_t s) {
     if (p.rows <= 0 || p.T <= 0) return;
     if (p.T <= 64) {

@@ -9,8 +9,9 @@ namespace cfm {
 namespace {
 
 // ---------------------------------------------------------------------------
-// Fused CFG combine + Euler update (VoiceHub "Custom Triton and CUDA kernels":
-// packed CFG combination plus an Euler update in one pass):
+// Fused CFG combine + Euler update (VoiceHub "Diffusion and flow TTS
+// optimization", section "Custom Triton and CUDA kernels", names the guidance
+// combine fused with the Euler step as a kernel worth writing):
 // x += sum_b (dt * w_b) * v_b, read once, written once; masked frames are
 // neither read nor written. Each thread owns EU float4s of x spaced one grid
 // apart (coalesced per instruction) and issues all of their loads before any

@@ -10,13 +10,12 @@
 //    WGM x WGN waves; K is staged BK at a time through two padded LDS buffers
 //    (global loads of the next stage issued at the top of an iteration, written
 //    to the other buffer at its end; fragments of k-step ks+1 read while the
-//    MFMAs of ks run). Small problems and fp32 A operands (rounded to bf16 while
-//    staging, so no conversion pass touches HBM).
-//  - gemm_dtl_kernel / gemm_dtlp_kernel: 256x256 tiles, operands loaded straight
-//    into an LDS ring by buffer_load ... lds, all waves in lockstep.
-//  - gemm_pp_kernel / gemm_pp64_kernel: the same loads, with the 8 waves in two
-//    groups that alternate load and multiply phases (ping-pong); K stage 32 or
-//    64. gemm_pp64_kernel is the default for large problems.
+//    MFMAs of ks run). Small and medium problems (128x128 and 64x64 tiles) and
+//    fp32 A operands (rounded to bf16 while staging, so no conversion pass
+//    touches HBM).
+//  - gemm_pp64_kernel: 256x256 tiles for large problems; operands loaded
+//    straight into an LDS ring by buffer_load ... lds, with the 8 waves in two
+//    groups that alternate load and multiply phases (ping-pong), K stage 64.
 // Every variant writes its output through the same per-wave LDS-staged
 // epilogues (epilogue.h).
 //
@@ -225,41 +224,23 @@ void launch_cfg(const AT* A, int lda, const bf16* W, int ldw, int M, int N, int 
 }
 
 // ---------------------------------------------------------------------------
-// Direct-to-LDS variant: operand tiles go from HBM straight into LDS
+// Large problems: operand tiles go from HBM straight into LDS
 // (buffer_load_dwordx4 ... lds: each lane's 16 bytes land at M0 + 16 * lane),
-// so no registers stage them and the pipeline runs deeper: a ring of 4 LDS
-// slots with K stage 32, the loads of stage k+3 issued while stage k is
-// multiplied. The loads are issued from inline assembly and their completion
-// is awaited explicitly (s_waitcnt vmcnt before the barrier that publishes a
-// stage), so the compiler neither knows about nor waits on them; the main loop
-// contains no other vector-memory instruction, and everything is drained before
-// the epilogue issues its own loads. M0 is written only by these sequences.
-// Rows are 64 bytes (unpadded); the four 16-byte chunks of a row are XOR-swizzled
-// by (row / 2) % 4 so that 8 consecutive rows read at the same k hit 8 distinct
-// bank groups.
-constexpr int DBK = 32;
-constexpr int NSLOT = 4;
-#ifndef SWZ_SHIFT
-#define SWZ_SHIFT 2
-#endif
-
-template <int BM_, int BN_, int WGM_, int WGN_, int NS_ = NSLOT>
-struct DCfg {
+// so no registers stage them. The loads are issued from inline assembly and
+// their completion is awaited explicitly (s_waitcnt vmcnt before the barrier
+// that publishes a stage), so the compiler neither knows about nor waits on
+// them; the main loop contains no other vector-memory instruction, and
+// everything is drained before the epilogue issues its own loads. M0 is written
+// only by these sequences (the compiler reserves M0 and sets it itself right
+// before each of its own uses; these kernels have none).
+template <int BM_, int BN_, int WGM_, int WGN_>
+struct PCfg {
     static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_;
-    static constexpr int NS = NS_;                                        // ring slots
     static constexpr int NW = WGM * WGN, NT = 64 * NW;
     static constexpr int WM = BM / WGM, WN = BN / WGN;
     static constexpr int TM = WM / 32, TN = WN / 32;
-    static constexpr int A_INSTR = BM / 16 / NW, W_INSTR = BN / 16 / NW;   // 16 rows per wave instruction
-    static constexpr int L = A_INSTR + W_INSTR;                           // loads per wave per stage
-    static constexpr int SLOT = (BM + BN) * DBK;                          // bf16 elements per slot
-    static constexpr int LDS_BYTES = NS * SLOT * 2;
-    static_assert(BM % (16 * NW) == 0 && BN % (16 * NW) == 0, "row groups");
     static_assert(TM >= 1 && TN >= 1, "wave tile");
-    static_assert(LDS_BYTES >= NW * EPI_WAVE_FLOATS * 4, "epilogue staging fits in the ring");
 };
-
-__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> SWZ_SHIFT) & 3); }
 
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, int voff, unsigned lds_addr) {
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
@@ -270,368 +251,6 @@ template <int N>
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory"); }
 
 __device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
-
-template <int INSTR>
-__device__ __forceinline__ void dma_stage(__amdgpu_buffer_rsrc_t rs, int ld, int rows_total, int K, int r0,
-                                          int k0, unsigned slot_addr, int wave, int lane) {
-#pragma unroll
-    for (int i = 0; i < INSTR; ++i) {
-        const int grp = wave * INSTR + i;              // 16-row group, wave-uniform
-        const int row = grp * 16 + (lane >> 2);
-        const int c = swz(row, lane & 3);              // logical chunk this lane fetches
-        const int r = r0 + row, k = k0 + c * 8;
-        const int off = (r < rows_total && k < K) ? (r * ld + k) * 2 : OOB;
-        dma16(rs, off, __builtin_amdgcn_readfirstlane(slot_addr + grp * 16 * DBK * 2));
-    }
-}
-
-template <typename C>
-__device__ __forceinline__ void dma_compute(f32x16 (&acc)[C::TM][C::TN], const bf16* as, const bf16* ws,
-                                            int wm, int wn, int li, int lh) {
-#pragma unroll
-    for (int ks = 0; ks < DBK / 16; ++ks) {
-        bf16x8 a[C::TM], b[C::TN];
-#pragma unroll
-        for (int i = 0; i < C::TM; ++i) {
-            const int row = wm * C::WM + i * 32 + li;
-            a[i] = *(const bf16x8*)(as + row * DBK + swz(row, ks * 2 + lh) * 8);
-        }
-#pragma unroll
-        for (int j = 0; j < C::TN; ++j) {
-            const int row = wn * C::WN + j * 32 + li;
-            b[j] = *(const bf16x8*)(ws + row * DBK + swz(row, ks * 2 + lh) * 8);
-        }
-#pragma unroll
-        for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-            for (int j = 0; j < C::TN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
-}
-
-template <typename C, int EPI>
-__global__ void __launch_bounds__(C::NT)
-gemm_dtl_kernel(const bf16* __restrict__ A, int lda, const bf16* __restrict__ W, int ldw,
-                int M, int N, int K, int tm, int tn, EpiParams ep) {
-    extern __shared__ __attribute__((aligned(16))) char smem[];
-    bf16* const ring = (bf16*)smem;           // NSLOT x [A: BM x DBK | W: BN x DBK]
-    const unsigned ring_addr = (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)smem;
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int li = lane & 31, lh = lane >> 5;
-    const int wm = wave / C::WGN, wn = wave % C::WGN;
-    int mt, nt;
-    tile_of(blockIdx.x, tm * tn, tm, tn, mt, nt);
-    const int m0 = mt * C::BM, n0 = nt * C::BN;
-    if (ep.m_dev) {
-        M = min(M, *ep.m_dev);
-        if (m0 >= M) return;
-    }
-    const __amdgpu_buffer_rsrc_t ra = rsrc_of(A, (long long)M * lda * 2);
-    const __amdgpu_buffer_rsrc_t rw = rsrc_of(W, (long long)N * ldw * 2);
-    const int nk = (K + DBK - 1) / DBK;
-
-    f32x16 acc[C::TM][C::TN];
-#pragma unroll
-    for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::TN; ++j) acc[i][j] = f32x16{};
-
-    auto issue = [&](int stage) {
-        const unsigned slot = ring_addr + (unsigned)((stage % NSLOT) * C::SLOT * 2);
-        dma_stage<C::A_INSTR>(ra, lda, M, K, m0, stage * DBK, slot, wave, lane);
-        dma_stage<C::W_INSTR>(rw, ldw, N, K, n0, stage * DBK, slot + C::BM * DBK * 2, wave, lane);
-    };
-
-    for (int st = 0; st < NSLOT - 1 && st < nk; ++st) issue(st);
-    for (int kt = 0; kt < nk; ++kt) {
-        // this wave's loads of stage kt are done once at most the later issued
-        // stages (up to two) are still in flight; the barrier then publishes
-        // every wave's part and also frees slot (kt + 3) % 4, read at kt - 1
-        const int ahead = min(nk - 1, kt + NSLOT - 2) - kt;
-        if (ahead >= 2) wait_vm<2 * C::L>();
-        else if (ahead == 1) wait_vm<C::L>();
-        else wait_vm<0>();
-        barrier_only();
-        if (kt + NSLOT - 1 < nk) issue(kt + NSLOT - 1);
-        const bf16* slot = ring + (kt % NSLOT) * C::SLOT;
-        dma_compute<C>(acc, slot, slot + C::BM * DBK, wm, wn, li, lh);
-    }
-    wait_vm<0>();
-    // epilogue through LDS, reusing the operand buffers (every wave is past its
-    // last read of them once it passes this barrier)
-    __syncthreads();
-    float* wl = (float*)smem + wave * EPI_WAVE_FLOATS;
-#pragma unroll
-    for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::TN; ++j)
-            epi_block<EPI>(ep, acc[i][j], wl, m0 + wm * C::WM + i * 32, n0 + wn * C::WN + j * 32, M, N, lane);
-}
-
-// Same ring of LDS slots, with the MFMA operand fragments read one stage
-// ahead: the barrier of iteration kt publishes stage kt + 1, whose fragments
-// are read into the second register set while the MFMAs of stage kt run on the
-// first, so no LDS latency sits between a barrier and the matrix cores. The two
-// register sets alternate through a loop unrolled by two. Slot reuse: the DMA
-// issued at iteration kt fills the slot of stage kt - 1, whose fragments every
-// wave consumed (in its MFMAs) during iteration kt - 1, before the barrier.
-template <typename C> struct Frags {
-    bf16x8 a[DBK / 16][C::TM], b[DBK / 16][C::TN];
-};
-
-template <typename C>
-__device__ __forceinline__ void read_frags(Frags<C>& f, const bf16* as, const bf16* ws, int wm, int wn, int li,
-                                           int lh) {
-#pragma unroll
-    for (int ks = 0; ks < DBK / 16; ++ks) {
-#pragma unroll
-        for (int i = 0; i < C::TM; ++i) {
-            const int row = wm * C::WM + i * 32 + li;
-            f.a[ks][i] = *(const bf16x8*)(as + row * DBK + swz(row, ks * 2 + lh) * 8);
-        }
-#pragma unroll
-        for (int j = 0; j < C::TN; ++j) {
-            const int row = wn * C::WN + j * 32 + li;
-            f.b[ks][j] = *(const bf16x8*)(ws + row * DBK + swz(row, ks * 2 + lh) * 8);
-        }
-    }
-}
-
-template <typename C>
-__device__ __forceinline__ void mma_frags(f32x16 (&acc)[C::TM][C::TN], const Frags<C>& f) {
-#pragma unroll
-    for (int ks = 0; ks < DBK / 16; ++ks)
-#pragma unroll
-        for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-            for (int j = 0; j < C::TN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[ks][i], f.b[ks][j], acc[i][j], 0, 0, 0);
-}
-
-// Reads the next stage's fragments into fn while multiplying fc, interleaved
-// (one LDS read, then a share of the MFMAs) so that LDS traffic is spread over
-// the whole stage instead of preceding it.
-template <typename C>
-__device__ __forceinline__ void read_mma(Frags<C>& fn, const bf16* as, const bf16* ws, int wm, int wn, int li,
-                                         int lh, f32x16 (&acc)[C::TM][C::TN], const Frags<C>& fc) {
-    read_frags<C>(fn, as, ws, wm, wn, li, lh);
-    mma_frags<C>(acc, fc);
-    constexpr int NR = (DBK / 16) * (C::TM + C::TN), NM = (DBK / 16) * C::TM * C::TN;
-    constexpr int PER = NM / NR;
-#pragma unroll
-    for (int i = 0; i < NR; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // one LDS read
-        __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);   // then PER MFMAs
-    }
-    if constexpr (NM - NR * PER > 0) __builtin_amdgcn_sched_group_barrier(0x008, NM - NR * PER, 0);
-}
-
-template <typename C, int EPI>
-__global__ void __launch_bounds__(C::NT)
-gemm_dtlp_kernel(const bf16* __restrict__ A, int lda, const bf16* __restrict__ W, int ldw,
-                 int M, int N, int K, int tm, int tn, EpiParams ep) {
-    extern __shared__ __attribute__((aligned(16))) char smem[];
-    bf16* const ring = (bf16*)smem;
-    const unsigned ring_addr = (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)smem;
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int li = lane & 31, lh = lane >> 5;
-    const int wm = wave / C::WGN, wn = wave % C::WGN;
-    int mt, nt;
-    tile_of(blockIdx.x, tm * tn, tm, tn, mt, nt);
-    const int m0 = mt * C::BM, n0 = nt * C::BN;
-    if (ep.m_dev) {
-        M = min(M, *ep.m_dev);
-        if (m0 >= M) return;
-    }
-    const __amdgpu_buffer_rsrc_t ra = rsrc_of(A, (long long)M * lda * 2);
-    const __amdgpu_buffer_rsrc_t rw = rsrc_of(W, (long long)N * ldw * 2);
-    const int nk = (K + DBK - 1) / DBK;
-
-    f32x16 acc[C::TM][C::TN];
-#pragma unroll
-    for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::TN; ++j) acc[i][j] = f32x16{};
-
-    auto issue = [&](int stage) {
-        const unsigned slot = ring_addr + (unsigned)((stage % C::NS) * C::SLOT * 2);
-        dma_stage<C::A_INSTR>(ra, lda, M, K, m0, stage * DBK, slot, wave, lane);
-        dma_stage<C::W_INSTR>(rw, ldw, N, K, n0, stage * DBK, slot + C::BM * DBK * 2, wave, lane);
-    };
-    auto slot_of = [&](int stage) { return ring + (stage % C::NS) * C::SLOT; };
-    // wait until at most `later` stages of this wave's loads are in flight
-    auto wait_stages = [&](int later) {
-        if constexpr (C::NS >= 5) { if (later >= 3) { wait_vm<3 * C::L>(); return; } }
-        if constexpr (C::NS >= 4) { if (later == 2) { wait_vm<2 * C::L>(); return; } }
-        if (later == 1) wait_vm<C::L>();
-        else wait_vm<0>();
-    };
-    // one iteration of a stage kt that has a successor: publish stage kt + 1,
-    // refill the ring, read stage kt + 1's fragments into fn while multiplying
-    // stage kt from fc
-    auto step = [&](int kt, const Frags<C>& fc, Frags<C>& fn) {
-        // stages kt + 2 .. kt + NS - 2 (those issued) may stay in flight
-        wait_stages(min(nk - 1, kt + C::NS - 2) - (kt + 1));
-        barrier_only();
-        if (kt + C::NS - 1 < nk) issue(kt + C::NS - 1);
-        const bf16* sl = slot_of(kt + 1);
-        read_mma<C>(fn, sl, sl + C::BM * DBK, wm, wn, li, lh, acc, fc);
-    };
-
-    for (int st = 0; st < C::NS - 1 && st < nk; ++st) issue(st);
-    wait_stages(min(nk, C::NS - 1) - 1);
-    barrier_only();
-    Frags<C> f0, f1;
-    read_frags<C>(f0, slot_of(0), slot_of(0) + C::BM * DBK, wm, wn, li, lh);
-    int kt = 0;
-    for (; kt + 2 < nk; kt += 2) {
-        step(kt, f0, f1);
-        step(kt + 1, f1, f0);
-    }
-    if (kt + 1 < nk) {   // two stages left
-        step(kt, f0, f1);
-        mma_frags<C>(acc, f1);
-    } else {             // one stage left
-        mma_frags<C>(acc, f0);
-    }
-    wait_vm<0>();
-    __syncthreads();
-    float* wl = (float*)smem + wave * EPI_WAVE_FLOATS;
-#pragma unroll
-    for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::TN; ++j)
-            epi_block<EPI>(ep, acc[i][j], wl, m0 + wm * C::WM + i * 32, n0 + wn * C::WN + j * 32, M, N, lane);
-}
-
-// Ping-pong schedule. The 8 waves form two groups of four (waves 0-3 and 4-7;
-// a CU deals a block's waves round-robin to its 4 SIMDs, so every SIMD holds
-// one wave of each group). Group g computes rows 128 g .. 128 g + 127 of the
-// tile, wave s of the group columns 64 s .. 64 s + 63. Every wave alternates a
-// memory phase M(k) (read stage k's fragments from LDS, issue its share of the
-// DMA of stage k + 3, wait for its reads) and a compute phase C(k) (16 MFMAs),
-// with a block barrier after each phase. Group 1 passes one extra barrier
-// before its first phase, so the groups are a phase apart: while one group's
-// waves multiply, the other group's waves on the same SIMDs load, and the
-// matrix cores are never waiting for LDS.
-//
-// Barrier order (b_i = i-th barrier after the prologue): group 0 runs
-// M(k) b_2k C(k) b_2k+1, group 1 runs M(k) between b_2k and b_2k+1 and C(k)
-// between b_2k+1 and b_2k+2; both pass 2 nk barriers. Stage k must be complete
-// before b_2k-1 (group 0 reads it after that barrier): group 0 waits for its
-// DMA share at the end of C(k - 1), group 1 at the end of M(k - 1). The DMA of
-// stage k + 3 refills the slot of stage k - 1, whose last reads (group 1's
-// M(k - 1)) completed before b_2k-1, and it is issued after that barrier by
-// both groups.
-template <typename C, int EPI>
-__global__ void __launch_bounds__(C::NT)
-gemm_pp_kernel(const bf16* __restrict__ A, int lda, const bf16* __restrict__ W, int ldw,
-               int M, int N, int K, int tm, int tn, EpiParams ep) {
-    static_assert(C::WGM == 2 && C::WGN == 4 && C::NS == 4, "two groups of four waves, four slots");
-    extern __shared__ __attribute__((aligned(16))) char smem[];
-    bf16* const ring = (bf16*)smem;
-    const unsigned ring_addr = (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)smem;
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int li = lane & 31, lh = lane >> 5;
-    // the group decides control flow around barriers: make it provably wave-uniform
-    const int grp = __builtin_amdgcn_readfirstlane(wave) / C::WGN, wn = wave % C::WGN;
-    int mt, nt;
-    tile_of(blockIdx.x, tm * tn, tm, tn, mt, nt);
-    const int m0 = mt * C::BM, n0 = nt * C::BN;
-    if (ep.m_dev) {
-        M = min(M, *ep.m_dev);
-        if (m0 >= M) return;   // whole block, before any barrier
-    }
-    const __amdgpu_buffer_rsrc_t ra = rsrc_of(A, (long long)M * lda * 2);
-    const __amdgpu_buffer_rsrc_t rw = rsrc_of(W, (long long)N * ldw * 2);
-    const int nk = (K + DBK - 1) / DBK;
-
-    f32x16 acc[C::TM][C::TN];
-#pragma unroll
-    for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::TN; ++j) acc[i][j] = f32x16{};
-
-    auto issue = [&](int stage) {
-        const unsigned slot = ring_addr + (unsigned)((stage % C::NS) * C::SLOT * 2);
-        dma_stage<C::A_INSTR>(ra, lda, M, K, m0, stage * DBK, slot, wave, lane);
-        dma_stage<C::W_INSTR>(rw, ldw, N, K, n0, stage * DBK, slot + C::BM * DBK * 2, wave, lane);
-    };
-    // this wave's DMA of stage s is complete once at most `later` younger
-    // stages are in flight
-    auto wait_stages = [&](int later) {
-        if (later >= 2) wait_vm<2 * C::L>();
-        else if (later == 1) wait_vm<C::L>();
-        else wait_vm<0>();
-    };
-    auto wait_next = [&](int k) {   // stage k + 1 complete (stages up to k + 3 issued)
-        if (k + 1 < nk) wait_stages(min(nk - 1, k + 3) - (k + 1));
-    };
-    auto sync = [&] {
-        __builtin_amdgcn_sched_barrier(0);
-        barrier_only();
-        __builtin_amdgcn_sched_barrier(0);
-    };
-    Frags<C> f;
-    auto mphase = [&](int k) {
-        const bf16* sl = ring + (k % C::NS) * C::SLOT;
-        read_frags<C>(f, sl, sl + C::BM * DBK, grp, wn, li, lh);
-        if (k + 3 < nk) issue(k + 3);
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    };
-
-    for (int st = 0; st < 3 && st < nk; ++st) issue(st);
-    wait_stages(min(nk, 3) - 1);
-    sync();
-    auto compute = [&] { mma_frags<C>(acc, f); };
-    if (grp == 0) {
-        for (int k = 0; k < nk; ++k) {
-            mphase(k);
-            sync();
-            compute();
-            wait_next(k);
-            sync();
-        }
-    } else {
-        for (int k = 0; k < nk; ++k) {
-            if (k == 0) sync();
-            mphase(k);
-            wait_next(k);
-            sync();
-            compute();
-            if (k + 1 < nk) sync();
-        }
-    }
-    // No block barrier before the epilogue: after its last barrier no wave reads
-    // the ring again (group 1's last multiply works from registers) and no load is
-    // in flight, so group 0 stages its output in its own 4 KiB area at once,
-    // while group 1 is still multiplying.
-    wait_vm<0>();
-    float* wl = (float*)smem + wave * EPI_WAVE_FLOATS;
-#pragma unroll
-    for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::TN; ++j)
-            epi_block<EPI>(ep, acc[i][j], wl, m0 + grp * C::WM + i * 32, n0 + wn * C::WN + j * 32, M, N, lane);
-}
-
-template <typename C, int EPI>
-void launch_pp(const bf16* A, int lda, const bf16* W, int ldw, int M, int N, int K,
-               const EpiParams& ep, hipStream_t s) {
-    const int tn = (N + C::BN - 1) / C::BN, tm = (M + C::BM - 1) / C::BM;
-    static const bool attr = [] {
-        return hipFuncSetAttribute((const void*)gemm_pp_kernel<C, EPI>,
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES) == hipSuccess;
-    }();
-    (void)attr;
-    gemm_pp_kernel<C, EPI><<<tm * tn, C::NT, C::LDS_BYTES, s>>>(A, lda, W, ldw, M, N, K, tm, tn, ep);
-}
 
 // Ping-pong with K stage 64 (tile 14): 128-byte LDS rows (one cache line per
 // row per stage, eight rows per load instruction), a 2-slot ring of 64 KiB
@@ -843,42 +462,10 @@ void launch_pp64(const bf16* A, int lda, const bf16* W, int ldw, int M, int N, i
     gemm_pp64_kernel<C, EPI><<<tm * tn, C::NT, LDS, s>>>(A, lda, W, ldw, M, N, K, tm, tn, ep);
 }
 
-template <typename C, int EPI>
-void launch_dcfgp(const bf16* A, int lda, const bf16* W, int ldw, int M, int N, int K,
-                  const EpiParams& ep, hipStream_t s) {
-    const int tn = (N + C::BN - 1) / C::BN, tm = (M + C::BM - 1) / C::BM;
-    static const bool attr = [] {
-        return hipFuncSetAttribute((const void*)gemm_dtlp_kernel<C, EPI>,
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES) == hipSuccess;
-    }();
-    (void)attr;
-    gemm_dtlp_kernel<C, EPI><<<tm * tn, C::NT, C::LDS_BYTES, s>>>(A, lda, W, ldw, M, N, K, tm, tn, ep);
-}
-
-template <typename C, int EPI>
-void launch_dcfg(const bf16* A, int lda, const bf16* W, int ldw, int M, int N, int K,
-                 const EpiParams& ep, hipStream_t s) {
-    const int tn = (N + C::BN - 1) / C::BN, tm = (M + C::BM - 1) / C::BM;
-    static const bool attr = [] {
-        return hipFuncSetAttribute((const void*)gemm_dtl_kernel<C, EPI>,
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES) == hipSuccess;
-    }();
-    (void)attr;
-    gemm_dtl_kernel<C, EPI><<<tm * tn, C::NT, C::LDS_BYTES, s>>>(A, lda, W, ldw, M, N, K, tm, tn, ep);
-}
-
-using D7 = DCfg<256, 256, 4, 2>;   // 8 waves, 64x128 per wave
-using D8 = DCfg<256, 256, 2, 2>;   // 4 waves, 128x128 per wave
-using D9 = DCfg<256, 256, 2, 4>;   // 8 waves, 128x64 per wave
-using D8P = DCfg<256, 256, 2, 2, 5>;   // 4 waves, 128x128 per wave, 5 slots (160 KiB)
-using D9P = DCfg<256, 256, 2, 4, 5>;   // 8 waves, 128x64 per wave, 5 slots
+using PP = PCfg<256, 256, 2, 4>;   // 8 waves in two groups of four, 128x64 per wave
 
 // tile configurations (index = the `tile` argument; 0 = automatic)
 using C1 = Cfg<128, 128, 32, 2, 2>;     // 4 waves, 64x64 per wave
-using C2 = Cfg<256, 256, 64, 2, 2>;     // 4 waves, 128x128 per wave
-using C3 = Cfg<256, 256, 32, 2, 4>;     // 8 waves, 128x64 per wave
-using C4 = Cfg<256, 128, 64, 2, 2>;     // 4 waves, 128x64 per wave
-using C5 = Cfg<256, 256, 64, 4, 2>;     // 8 waves, 64x128 per wave
 using C6 = Cfg<128, 128, 64, 2, 2>;     // 4 waves, 64x64 per wave, deeper K stage
 using C10 = Cfg<64, 64, 64, 2, 2>;      // 4 waves, 32x32 per wave: small problems
 using CF = Cfg<128, 128, 32, 2, 2>;     // fp32 A operands
@@ -898,19 +485,9 @@ void launch_epi(int tile, const AT* A, int lda, const bf16* W, int ldw, int M, i
             tile = big >= 192 ? (N >= 1024 || K >= 1024 ? 14 : 1) : mid >= 160 ? 6 : 10;
         }
         switch (tile) {
-            case 2: launch_cfg<C2, AT, EPI>(A, lda, W, ldw, M, N, K, ep, s); break;
-            case 3: launch_cfg<C3, AT, EPI>(A, lda, W, ldw, M, N, K, ep, s); break;
-            case 4: launch_cfg<C4, AT, EPI>(A, lda, W, ldw, M, N, K, ep, s); break;
-            case 5: launch_cfg<C5, AT, EPI>(A, lda, W, ldw, M, N, K, ep, s); break;
             case 6: launch_cfg<C6, AT, EPI>(A, lda, W, ldw, M, N, K, ep, s); break;
-            case 7: launch_dcfg<D7, EPI>(A, lda, W, ldw, M, N, K, ep, s); break;
-            case 8: launch_dcfg<D8, EPI>(A, lda, W, ldw, M, N, K, ep, s); break;
-            case 9: launch_dcfg<D9, EPI>(A, lda, W, ldw, M, N, K, ep, s); break;
             case 10: launch_cfg<C10, AT, EPI>(A, lda, W, ldw, M, N, K, ep, s); break;
-            case 11: launch_dcfgp<D8P, EPI>(A, lda, W, ldw, M, N, K, ep, s); break;
-            case 12: launch_dcfgp<D9P, EPI>(A, lda, W, ldw, M, N, K, ep, s); break;
-            case 13: launch_pp<D9, EPI>(A, lda, W, ldw, M, N, K, ep, s); break;
-            case 14: launch_pp64<D9, EPI>(A, lda, W, ldw, M, N, K, ep, s); break;
+            case 14: launch_pp64<PP, EPI>(A, lda, W, ldw, M, N, K, ep, s); break;
             default: launch_cfg<C1, AT, EPI>(A, lda, W, ldw, M, N, K, ep, s); break;
         }
     }

@@ -46,7 +46,8 @@ struct EpiParams {
 };
 
 // bf16 MFMA GEMM, A bf16 or f32 (rounded to bf16 while staging), W bf16 [N, K].
-// tile: 0 = pick by problem size, 1 = 128x128, 2 = 256x256 (bf16 A only)
+// tile: 0 = pick by problem size; 1 = 128x128, 6 = 128x128 with K stage 64, 10 = 64x64,
+// 14 = 256x256 ping-pong (bf16 A only above 1)
 void launch_gemm_bf16(bool a_f32, int epi, const void* A, int lda, const bf16* W, int ldw,
                       int M, int N, int K, const EpiParams& ep, hipStream_t s, int tile = 0);
 // fp32 SIMT GEMM, A f32 (optionally SiLU on load), W f32 or bf16 [N, K]; EPI_ACT stores f32.
@@ -73,6 +74,8 @@ struct AttnParams {
     const int32_t* row_off = nullptr;
 };
 void launch_attention_bf16(const AttnParams& p, hipStream_t s);
+// whether the bf16 attention's LDS (key ring plus per-key tables) holds sequences of T keys
+bool attention_bf16_fits(long long T);
 void launch_attention_f32(const AttnParams& p, hipStream_t s);
 
 // adaLN LayerNorm: output token o = row*Tout + t reads input token row*Tin + off + t.

@@ -80,6 +80,22 @@ cfm_status check_config(const cfm_config* c) {
             cond_rows * std::max(c->cond_dim, c->latent_dim) * 4 >= kMaxOperandBytes)
             return fail(CFM_E_UNSUPPORTED, "capacity too large: an activation operand would exceed 2 GiB");
     }
+    {
+        // launch limits of the kernels a call enqueues: rejected here so that a call
+        // never fails half-way through its launch sequence
+        const long long P = c->cond_mode == CFM_COND_PREFIX ? c->n_prefix : 0;
+        const long long rows = (long long)c->n_branches * c->max_requests;
+        if (rows > 65535 || c->n_heads > 65535)
+            return fail(CFM_E_UNSUPPORTED, "n_branches * max_requests and n_heads must be <= 65535 (attention grid)");
+        if (c->max_steps > 65535) return fail(CFM_E_UNSUPPORTED, "max_steps must be <= 65535");
+        if (c->spk_dim > 0 && c->max_requests + 1LL > 65535)
+            return fail(CFM_E_UNSUPPORTED, "max_requests must be < 65535 with a speaker path");
+        if ((long long)c->max_requests * P > 65535)
+            return fail(CFM_E_UNSUPPORTED, "max_requests * n_prefix must be <= 65535");
+        if (c->dtype == CFM_BF16 && !attention_bf16_fits(c->max_frames + P))
+            return fail(CFM_E_UNSUPPORTED, "max_frames + n_prefix = %lld: the attention key tables exceed LDS",
+                        (long long)c->max_frames + P);
+    }
     if (c->cond_mode == CFM_COND_PREFIX) {
         if (c->n_prefix <= 0) return fail(CFM_E_UNSUPPORTED, "prefix mode needs n_prefix > 0");
         if (c->cond_dim != c->latent_dim) return fail(CFM_E_UNSUPPORTED, "prefix mode needs cond_dim == latent_dim");
@@ -624,15 +640,17 @@ cfm_status cfm_gemm_bf16(const void* A, int a_is_f32, int lda, const void* W, in
                          const float* bias, int M, int N, int K, int epilogue,
                          const float* gate, void* C, int ldc, int tile, void* stream) {
     if (M < 0 || N < 0 || K < 0) return fail(CFM_E_VALUE, "negative size");
-    if (tile < 0 || tile > 14 || (tile > 1 && a_is_f32)) return fail(CFM_E_VALUE, "tile %d", tile);
+    if (!(tile == 0 || tile == 1 || tile == 6 || tile == 10 || tile == 14) || (tile > 1 && a_is_f32))
+        return fail(CFM_E_VALUE, "tile %d", tile);
     if (epilogue < 0 || epilogue > 3) return fail(CFM_E_VALUE, "epilogue %d", epilogue);
     if (M == 0 || N == 0) return CFM_OK;
     if (A == nullptr || W == nullptr || C == nullptr) return fail(CFM_E_NULL, "A, W or C is NULL");
     if (epilogue == 3 && gate == nullptr) return fail(CFM_E_NULL, "gate is NULL");
     const int kq = a_is_f32 ? 4 : 8;
-    if (K % kq || lda % kq || ldw % 8 || lda < K || ldw < round8(K) || ldc < N)
+    if (K % kq || lda % kq || ldw % 8 || lda < K || ldw < round8(K) || ldc < N || (N > 3 && ldc % 4))
         return fail(CFM_E_SHAPE, "K/lda/ldw/ldc do not meet the layout rules");
-    if (!aligned16(A) || !aligned16(W)) return fail(CFM_E_SHAPE, "A and W must be 16-byte aligned");
+    if (!aligned16(A) || !aligned16(W) || !aligned16(C) || (bias && !aligned16(bias)) || (gate && !aligned16(gate)))
+        return fail(CFM_E_SHAPE, "A, W, C, bias and gate must be 16-byte aligned");
     if ((long long)M * lda * (a_is_f32 ? 4 : 2) >= kMaxOperandBytes || (long long)N * ldw * 2 >= kMaxOperandBytes)
         return fail(CFM_E_SHAPE, "operand above 2 GiB");
     static const int map[4] = {EPI_F32, EPI_ACT, EPI_GELU_ACT, EPI_GATED};

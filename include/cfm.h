@@ -116,8 +116,15 @@ int cfm_weight_manifest(const cfm_config* cfg, cfm_tensor_desc* out, int cap);
 /* Creates a sampler context (host memory only; no HIP call). BORROWS
  * `weights` (cfm_weights_bytes, filled per the manifest) and `workspace`
  * (cfm_workspace_bytes): both are caller-owned device memory that must outlive
- * the context and every call still in flight. Errors: CFM_E_NULL,
- * CFM_E_UNSUPPORTED, CFM_E_VALUE, CFM_E_WORKSPACE. */
+ * the context and every call still in flight. All state of a call lives in that
+ * caller-visible workspace and the library allocates nothing, the condition the
+ * vox-serve page "Adding a Model" sets for graph-captured model code (buffers
+ * allocated up front, shapes taken from arguments, no allocation in the captured
+ * region). The config is validated here, so that an unsupported request fails
+ * before anything is mutated (VoiceHub "Diffusion and flow TTS optimization",
+ * section "Attention": an explicit request the backend cannot honour fails
+ * before model mutation). Errors: CFM_E_NULL, CFM_E_UNSUPPORTED, CFM_E_VALUE,
+ * CFM_E_WORKSPACE, CFM_E_SHAPE (weights or workspace not 256-byte aligned). */
 cfm_status cfm_create(const cfm_config* cfg, const void* weights, void* workspace,
                       size_t workspace_bytes, cfm_ctx** out_ctx);
 
@@ -131,12 +138,32 @@ cfm_status cfm_create(const cfm_config* cfg, const void* weights, void* workspac
  * Tx = n_frames. R == 0 is a no-op; S == 0 gives out = x0. A request with no
  * valid frame gives out = x0. Inputs must stay alive and unmodified until the
  * stream has passed this call. Errors: CFM_E_NULL, CFM_E_SHAPE, CFM_E_CAPACITY,
- * CFM_E_VALUE (negative count, non-finite scale), CFM_E_HIP. */
+ * CFM_E_VALUE (negative count, non-finite scale), CFM_E_HIP.
+ * Sources of the contract:
+ *   - every request's CFG rows go through ONE estimator call per step (the
+ *     vLLM-Omni TTS blog, section "CFM/LocDiT decode-tail batching", batches the
+ *     two CFG rows of many requests into one estimator call);
+ *   - the step loop has no host synchronisation: step sizes and guidance
+ *     weights are computed on the host before enqueue and passed by value (the
+ *     same section removes the per-step host syncs of the Euler loop);
+ *   - nothing is allocated and every shape comes from the arguments (vox-serve,
+ *     "Adding a Model": graph-capture rules), so the call can be captured;
+ *   - packed CFG rows give what separate branch calls give, and padded frames
+ *     are fully masked and returned untouched (VoiceHub "Diffusion and flow TTS
+ *     optimization", table "Semantic-preserving and approximate changes");
+ *   - randomness belongs to the request: the noise x0 is an input and the
+ *     library draws no random numbers (vox-serve, "Adding a Model"; the
+ *     Breeze-TTS-2 recipe's per-request generators);
+ *   - arguments are validated before anything is enqueued, so a rejected call
+ *     leaves out untouched (VoiceHub, section "Attention"). */
 cfm_status cfm_sample(cfm_ctx* ctx, const float* x0, const float* cond, const float* spk,
                       const uint8_t* frame_mask, int n_requests, int n_frames, int n_steps,
                       const float* guidance, float* out, void* stream);
 
-/* Frees host state only (the borrowed buffers stay the caller's). NULL-safe. */
+/* Frees host state only: the borrowed weight and workspace buffers stay the
+ * caller's (vox-serve, "Adding a Model": buffers are owned by the caller and
+ * outlive the captured work). Work already enqueued keeps using them, so the
+ * caller frees them only after the stream has passed its last call. NULL-safe. */
 void cfm_destroy(cfm_ctx* ctx);
 
 const char* cfm_status_string(cfm_status s);
@@ -163,8 +190,9 @@ cfm_status cfm_profile_disable(cfm_ctx* ctx);
  * Single-kernel entry points (the same kernels cfm_sample launches), for
  * kernel-level parity tests and roofline measurement.
  *
- * Fused CFG combine + Euler update (VoiceHub, "Custom Triton and CUDA kernels":
- * packed CFG combination plus an Euler update):
+ * Fused CFG combine + Euler update (VoiceHub "Diffusion and flow TTS optimization",
+ * section "Custom Triton and CUDA kernels", lists the guidance combine fused with
+ * the Euler step among the kernels worth writing):
  *   for every valid frame (r, t): x[r,t,:] += dt * sum_b w[b] * v[b,r,t,:]
  * v device fp32 [nb, R, Tx, C]; w host fp32 [nb] branch weights (for guidance
  * scale s: w = (1 - s, s); three branches: (1 - s_t, s_t - s_s, s_s));
@@ -180,14 +208,15 @@ cfm_status cfm_cfg_euler(const float* v, const float* w, int nb, float dt, const
  *   3: gated residual C(fp32) += gate[n] * (acc + bias[n]) with gate device fp32 [N].
  * K % 8 == 0 (bf16 A) or K % 4 == 0 (fp32 A); lda, ldw multiples of 8 (bf16)
  * or 4 (fp32 A); ldw >= K rounded up to 8 with zero padding.
- * tile: 0 = chosen from the problem size (what cfm_sample uses); 1..14 force
- * one tile configuration (1 = 128x128, 2..5 = 256x256 / 256x128 register-staged,
- * 6 = 128x128 with K stage 64, 7..9 = 256x256 direct-to-LDS, 10 = 64x64,
- * 11..12 = 256x256 direct-to-LDS with operand fragments read a stage ahead,
- * 13 = 256x256 direct-to-LDS, two wave groups alternating loads and MFMAs,
- * 14 = as 13 with a K stage of 64); a value outside 0..14 returns
- * CFM_E_VALUE, as does a tile above 1 with an fp32 A operand. The GELU of epilogue 2 is
- * evaluated with an erfc approximation of relative error below 1e-5 (bf16 rounding: 2^-9). */
+ * tile: 0 = chosen from the problem size (what cfm_sample uses); 1 = 128x128
+ * tiles, 6 = 128x128 with a K stage of 64, 10 = 64x64, 14 = 256x256 with two
+ * wave groups alternating loads and MFMAs (K stage 64). Any other value returns
+ * CFM_E_VALUE, as does a tile other than 0 or 1 with an fp32 A operand. The GELU
+ * of epilogue 2 is evaluated with an erfc approximation of relative error below
+ * 1e-5 (bf16 rounding: 2^-9).
+ * Layout rules (CFM_E_SHAPE otherwise): ldc >= N, and ldc % 4 == 0 when N > 3
+ * (rows of four or more columns are written with vector stores); A, W, C, bias
+ * and gate 16-byte aligned. */
 cfm_status cfm_gemm_bf16(const void* A, int a_is_f32, int lda, const void* W, int ldw,
                          const float* bias, int M, int N, int K, int epilogue,
                          const float* gate, void* C, int ldc, int tile, void* stream);

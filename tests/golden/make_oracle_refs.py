@@ -5,9 +5,13 @@ tests at full size compare the HIP sampler against these stored values (the
 oracle needs minutes to hours per full workload, too long for a test).
 
 For each workload a few requests are run through the whole oracle sampler
-(requests never interact, so a subset is exact), and every ``STRIDE``-th frame
-of their outputs is stored as float32 together with the sha256 of the oracle
-source it came from. Run from the repository root:
+(requests never interact, so a subset is exact). Their outputs are stored as
+float32 together with the sha256 of the oracle source they came from: every
+frame when a request has at most ``ALL_FRAMES`` frames (the LocDiT decode tail's
+four patch frames), else every ``STRIDE``-th frame. The requests are chosen to
+reach the row-dependent paths of the batched layout: the last request of a
+batch, a packed row that starts past 16k tokens, speaker-branch rows of
+requests other than the first. Run from the repository root:
 
     python tests/golden/make_oracle_refs.py [workload ...]
 """
@@ -28,6 +32,7 @@ from oracle import sampler as O  # noqa: E402
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 STRIDE = 4
+ALL_FRAMES = 64
 
 
 def oracle_hash() -> str:
@@ -37,14 +42,16 @@ def oracle_hash() -> str:
 
 def chosen_requests(s, inputs) -> list:
     if s.name == "locdit_tail":
-        return [0, 37, 63]
+        return [0, 21, 37, 63]
     if s.name == "varlen_masked":
+        # shortest, longest, and request 26, whose packed unconditional row
+        # starts past token 16384 (its conditional row past 40k)
         L = inputs["lengths"]
-        return sorted({int(np.argmin(L)), int(np.argmax(L)), 7})
+        return sorted({int(np.argmin(L)), int(np.argmax(L)), 7, 26})
     if s.name == "mel_dit":
-        return [0, 5]
+        return [0, 5, 7]
     if s.name == "multicond_rf":
-        return [0, 11]
+        return [0, 6, 11]
     return list(range(s.n_requests))
 
 
@@ -56,7 +63,7 @@ def make(name: str) -> str:
     t0 = time.time()
     out = O.sample(W, s, I["x0"], I["cond"], I["spk"], I["mask"], s.n_steps, s.guidance,
                    requests=reqs, workers=min(len(reqs), O.host_cores()))
-    frames = np.arange(0, s.n_frames, STRIDE)
+    frames = np.arange(s.n_frames) if s.n_frames <= ALL_FRAMES else np.arange(0, s.n_frames, STRIDE)
     path = os.path.join(HERE, f"oracle_{name}.npz")
     np.savez_compressed(path, out=out[:, frames, :].astype(np.float32), requests=np.array(reqs),
                         frames=frames, oracle_sha256=np.array(oracle_hash()))

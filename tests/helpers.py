@@ -8,13 +8,7 @@ import synth
 
 def config_for(s: "synth.CfmShape", **cap):
     import flow_matching_tts_amd as F
-    return F.make_config(
-        n_layers=s.n_layers, d_model=s.d_model, n_heads=s.n_heads, ffn_dim=s.ffn_dim,
-        latent_dim=s.latent_dim, cond_dim=s.cond_dim, cond_mode=s.cond_mode, n_prefix=s.n_prefix,
-        spk_dim=s.spk_dim, n_branches=s.n_branches, dtype=s.dtype, t_freq_dim=s.t_freq_dim,
-        max_requests=cap.get("max_requests", s.n_requests),
-        max_frames=cap.get("max_frames", s.n_frames),
-        max_steps=cap.get("max_steps", s.n_steps))
+    return F.config_from_shape(s, **cap)
 
 
 def dev(a, dtype=None):

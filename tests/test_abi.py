@@ -156,3 +156,124 @@ def test_single_kernel_entry_validation(lib):
     f = 1 << 20
     assert lib.cfm_attention_bf16(f, f, f, None, 2, 8, 1, f, 10, f, None) == 6
     assert lib.cfm_adaln(1 << 20, 1 << 21, 1 << 22, 4, 30, 0, 1 << 23, None) == 2
+
+
+def test_config_launch_limits_rejected_at_create(lib):
+    """Configs whose kernels could not be launched are refused when the context is
+    created (and by the size queries), never half-way through a sampling call."""
+    fake = 1 << 20
+    ctx = C.c_void_p()
+    small = dict(d_model=64, n_heads=1, ffn_dim=64)
+    cases = [
+        (dict(small, n_requests=40000, n_frames=1), b"attention grid"),   # 80000 branch rows
+        (dict(n_steps=70000), b"max_steps"),                              # timestep-embedding grid
+        (dict(n_frames=100000, n_requests=1), b"LDS"),                    # attention key tables
+    ]
+    for kw, why in cases:
+        cfg = _cfg(**kw)
+        assert lib.cfm_workspace_bytes(C.byref(cfg)) == 0, kw
+        assert lib.cfm_create(C.byref(cfg), fake, fake, 1 << 40, C.byref(ctx)) == 5, kw
+        assert why in lib.cfm_last_error_detail(), (kw, lib.cfm_last_error_detail())
+    prefix = config_for(synth.workload("locdit_tail").replace(n_requests=17000, d_model=512, n_heads=8,
+                                                               ffn_dim=1024))
+    assert lib.cfm_create(C.byref(prefix), fake, fake, 1 << 40, C.byref(ctx)) == 5
+    assert b"n_prefix" in lib.cfm_last_error_detail()
+    ok = _cfg(n_frames=90000, n_requests=1)        # still inside the LDS budget
+    assert lib.cfm_workspace_bytes(C.byref(ok)) > 0
+
+
+def test_gemm_entry_rejects_misaligned_outputs(lib):
+    a, w, c = 1 << 20, 1 << 21, 1 << 22
+    ok = lambda **k: lib.cfm_gemm_bf16(k.get("A", a), 0, 16, w, 16, k.get("bias", None), 4, 4, 16,
+                                       k.get("epi", 0), k.get("gate", None), k.get("C", c),
+                                       k.get("ldc", 4), k.get("tile", 0), None)
+    assert ok(ldc=6) == 2                 # ldc % 4 != 0: the vector epilogues need 16-byte rows
+    assert ok(C=c + 8) == 2
+    assert ok(bias=c + 4) == 2
+    assert ok(epi=3, gate=c + 4) == 2
+    assert ok(tile=2) == 4 and ok(tile=13) == 4 and ok(tile=15) == 4   # tiles the library does not have
+
+
+def test_binding_rejects_bad_shapes_before_any_launch():
+    import torch
+    import flow_matching_tts_amd as F
+    s = synth.workload("multicond_rf").replace(n_requests=2, n_frames=10, n_steps=3)
+    cfg = config_for(s)
+    R, Tx = 2, 10
+    x0 = torch.zeros(R, Tx, s.latent_dim)
+    cond = torch.zeros(R, Tx, s.cond_dim)
+    spk = torch.zeros(R, s.spk_dim)
+    good = dict(x0=x0, cond=cond, spk=spk, n_steps=3, guidance=(3.0, 1.5))
+
+    def bad(**kw):
+        args = dict(good, **kw)
+        with pytest.raises(ValueError) as e:
+            F.check_sample_args(cfg, args["x0"], args["cond"], args.get("mask"), args.get("spk"),
+                                args.get("out"), args["n_steps"], args["guidance"])
+        return str(e.value)
+
+    assert "x0" in bad(x0=torch.zeros(R, Tx, s.latent_dim + 4))
+    assert "cond" in bad(cond=torch.zeros(R, Tx - 1, s.cond_dim))
+    assert "cond" in bad(cond=torch.zeros(R, Tx, s.cond_dim, dtype=torch.float64))
+    assert "mask" in bad(mask=torch.ones(R, Tx + 1, dtype=torch.uint8))
+    assert "mask" in bad(mask=torch.ones(R, Tx, dtype=torch.int32))
+    assert "spk" in bad(spk=None)
+    assert "spk" in bad(spk=torch.zeros(R, s.spk_dim - 4))
+    assert "out" in bad(out=torch.zeros(R, Tx - 1, s.latent_dim))
+    assert "guidance" in bad(guidance=(2.0,))
+    assert "capacity" in bad(n_steps=4)
+    assert "contiguous" in bad(x0=torch.zeros(R, s.latent_dim, Tx).transpose(1, 2))
+    # every shape right: only the device is wrong (host tensors here)
+    assert "CUDA" in bad()
+    prefix = synth.workload("locdit_tail").replace(n_requests=2)
+    pcfg = config_for(prefix)
+    with pytest.raises(ValueError, match="cond"):
+        F.check_sample_args(pcfg, torch.zeros(2, 4, 64), torch.zeros(2, 4, 64 + 4), n_steps=1,
+                            guidance=(2.0,))
+    with pytest.raises(ValueError, match="no speaker"):
+        F.check_sample_args(config_for(synth.workload("mel_dit")), torch.zeros(1, 5, 100),
+                            torch.zeros(1, 5, 512), spk=torch.zeros(1, 4), n_steps=1, guidance=(2.0,))
+
+
+def test_single_kernel_wrappers_reject_bad_shapes_before_any_launch():
+    import torch
+    import flow_matching_tts_amd as F
+    bf = torch.bfloat16
+    with pytest.raises(ValueError, match="x"):
+        F.cfg_euler(torch.zeros(2, 3, 5, 8), [0.5, 0.5], 0.1, torch.zeros(3, 5, 4))
+    with pytest.raises(ValueError, match="weights"):
+        F.cfg_euler(torch.zeros(2, 3, 5, 8), [1.0], 0.1, torch.zeros(3, 5, 8))
+    with pytest.raises(ValueError, match="mask"):
+        F.cfg_euler(torch.zeros(2, 3, 5, 8), [0.5, 0.5], 0.1, torch.zeros(3, 5, 8),
+                    mask=torch.ones(3, 4, dtype=torch.uint8))
+    A, W = torch.zeros(10, 16, dtype=bf), torch.zeros(12, 16, dtype=bf)
+    with pytest.raises(ValueError, match="columns"):
+        F.gemm_bf16(A, W, epilogue=0, out=torch.zeros(10, 8))
+    with pytest.raises(ValueError, match="out"):
+        F.gemm_bf16(A, W, epilogue=0, out=torch.zeros(9, 12))
+    with pytest.raises(ValueError, match="out"):
+        F.gemm_bf16(A, W, epilogue=1, out=torch.zeros(10, 12))           # bf16 epilogue, fp32 out
+    with pytest.raises(ValueError, match="bias"):
+        F.gemm_bf16(A, W, torch.zeros(11), epilogue=0, out=torch.zeros(10, 12))
+    with pytest.raises(ValueError, match="gate"):
+        F.gemm_bf16(A, W, epilogue=3, out=torch.zeros(10, 12))
+    with pytest.raises(ValueError, match="K"):
+        F.gemm_bf16(A, W, epilogue=0, out=torch.zeros(10, 12), K=24)
+    qk = torch.zeros(2, 70, 2 * 64, dtype=bf)
+    vt = torch.zeros(2, 1, 64, 128, dtype=bf)
+    kv = torch.zeros(2, dtype=torch.int32)
+    o = torch.zeros(2, 70, 64, dtype=bf)
+    with pytest.raises(ValueError, match="vt"):
+        F.attention_bf16(qk, torch.zeros(2, 1, 64, 70, dtype=bf), kv, o, n_heads=1)
+    with pytest.raises(ValueError, match="kv_len"):
+        F.attention_bf16(qk, vt, torch.zeros(3, dtype=torch.int32), o, n_heads=1)
+    with pytest.raises(ValueError, match="o"):
+        F.attention_bf16(qk, vt, kv, torch.zeros(2, 69, 64, dtype=bf), n_heads=1)
+    with pytest.raises(ValueError, match="qk"):
+        F.attention_bf16(qk, vt, kv, o, n_heads=2)
+    with pytest.raises(ValueError, match="CUDA"):
+        F.attention_bf16(qk, vt, kv, o, n_heads=1)
+    with pytest.raises(ValueError, match="shift"):
+        F.adaln(torch.zeros(5, 64), torch.zeros(60), torch.zeros(64), torch.zeros(5, 64))
+    with pytest.raises(ValueError, match="y"):
+        F.adaln(torch.zeros(5, 64), torch.zeros(64), torch.zeros(64), torch.zeros(5, 32))

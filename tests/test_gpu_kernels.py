@@ -86,7 +86,7 @@ def _gemm_ref(A, W, bias, epi, gate=None, c0=None):
 @pytest.mark.parametrize("M,N,K", [(300, 200, 136), (128, 128, 64), (1, 3, 8), (1000, 100, 1024), (257, 3072, 1024),
                                    (520, 600, 2048)])
 @pytest.mark.parametrize("epi", [0, 1, 2, 3])
-@pytest.mark.parametrize("tile", [1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14])
+@pytest.mark.parametrize("tile", [0, 1, 6, 10, 14])
 def test_gemm_bf16_epilogues(M, N, K, epi, tile):
     import flow_matching_tts_amd as F
     rng = np.random.default_rng(M * 7 + N + K + epi)
@@ -169,9 +169,16 @@ def test_attention_bf16_matches_oracle(rows, T, H):
     _attn_call(qkv, H, kv_len, o, mask)
     got = o.float().cpu().numpy()
     want = _attn_ref(qkv, H, valid)
+    # Per element: o = sum_k p_k v_k / sum_k p_k with each p_k rounded to bf16 before
+    # the P.V product (relative error <= 2^-8) and o rounded to bf16 on store (<= 2^-8
+    # of |o|), so |o - o_ref| <= 2^-8 (max_k |v_k| + |o_ref|), max over the valid keys
+    # of that row, head and head dimension; 1.5x margin for the fp32 score and sum.
+    d = H * 64
+    v = np.abs(qkv[..., 2 * d:]).reshape(rows, T, d)
+    vmax = np.where(valid[:, :, None], v, 0.0).max(axis=1, keepdims=True)     # [rows, 1, d]
+    bound = 1.5 * 2.0 ** -8 * (vmax + np.abs(want)) + 1e-6
     err = np.abs(got - want)
-    # P is rounded to bf16 before P.V and o is stored in bf16: a few bf16 ulps of max|v|
-    assert err.max() < 0.03 * np.abs(qkv).max(), err.max()
+    assert np.all(err <= bound), (err.max(), float((err / bound).max()))
     rel = np.linalg.norm(got - want) / np.linalg.norm(want)
     assert rel < 6e-3, rel
 
