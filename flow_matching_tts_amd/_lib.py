@@ -25,7 +25,7 @@ KERNEL_CLASSES = {"gemm_qkv": 0, "gemm_proj": 1, "gemm_fc1": 2, "gemm_fc2": 3, "
 EXPORTS = ["cfm_weights_bytes", "cfm_workspace_bytes", "cfm_weight_manifest", "cfm_create",
            "cfm_sample", "cfm_destroy", "cfm_status_string", "cfm_last_error_detail",
            "cfm_profile_enable", "cfm_profile_read", "cfm_profile_disable", "cfm_cfg_euler",
-           "cfm_gemm_bf16", "cfm_attention_bf16", "cfm_adaln"]
+           "cfm_gemm_bf16", "cfm_attention_bf16", "cfm_attention_bf16_noalloc", "cfm_adaln"]
 
 
 class cfm_config(C.Structure):
@@ -89,6 +89,8 @@ def load() -> C.CDLL:
     lib.cfm_gemm_bf16.restype = i32
     lib.cfm_attention_bf16.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp, C.c_size_t, vp, vp]
     lib.cfm_attention_bf16.restype = i32
+    lib.cfm_attention_bf16_noalloc.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp, vp]
+    lib.cfm_attention_bf16_noalloc.restype = i32
     lib.cfm_adaln.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp]
     lib.cfm_adaln.restype = i32
     _lib = lib
@@ -345,11 +347,8 @@ def gemm_bf16(A, W, bias=None, *, epilogue: int, out, gate=None, K: Optional[int
     return out
 
 
-def attention_bf16(qk, vt, kv_len, o, *, n_heads: int, key_mask=None, stream=None):
-    """qk bf16 [rows, T, 2*H*64], vt bf16 [rows, H, 64, Tp] (Tp = T rounded up to 64),
-    kv_len int32 [rows], key_mask uint8 [rows, T] or None, o bf16 [rows, T, H*64]."""
+def _check_attention(qk, vt, kv_len, o, H, key_mask):
     import torch
-    H = int(n_heads)
     if len(qk.shape) != 3:
         raise ValueError(f"qk must be [rows, T, 2*H*64], got shape {_shape(qk)}")
     rows, T = int(qk.shape[0]), int(qk.shape[1])
@@ -360,9 +359,28 @@ def attention_bf16(qk, vt, kv_len, o, *, n_heads: int, key_mask=None, stream=Non
     _need("key_mask", key_mask, (rows, T), torch.uint8, optional=True)
     _need("o", o, (rows, T, H * 64), torch.bfloat16)
     _on_device(qk=qk, vt=vt, kv_len=kv_len, key_mask=key_mask, o=o)
+    return rows, T, Tp
+
+
+def attention_bf16(qk, vt, kv_len, o, *, n_heads: int, key_mask=None, stream=None):
+    """qk bf16 [rows, T, 2*H*64], vt bf16 [rows, H, 64, Tp] (Tp = T rounded up to 64),
+    kv_len int32 [rows], key_mask uint8 [rows, T] or None, o bf16 [rows, T, H*64]."""
+    import torch
+    H = int(n_heads)
+    rows, T, Tp = _check_attention(qk, vt, kv_len, o, H, key_mask)
     scratch = torch.empty(rows * 4 + rows * Tp + rows * (Tp // 64) + 64, dtype=torch.uint8, device=qk.device)
     check(load().cfm_attention_bf16(_ptr(qk), _ptr(vt), _ptr(kv_len), _ptr(key_mask), rows, T,
                                     H, _ptr(scratch), scratch.numel(), _ptr(o), _stream(stream)))
+    return o
+
+
+def attention_bf16_noalloc(qk, vt, kv_len, o, *, n_heads: int, key_mask=None, stream=None):
+    """attention_bf16 through the entry point that allocates nothing (its key tables
+    live in the library's own per-GPU buffer)."""
+    H = int(n_heads)
+    rows, T, _ = _check_attention(qk, vt, kv_len, o, H, key_mask)
+    check(load().cfm_attention_bf16_noalloc(_ptr(qk), _ptr(vt), _ptr(kv_len), _ptr(key_mask), rows, T,
+                                            H, _ptr(o), _stream(stream)))
     return o
 
 

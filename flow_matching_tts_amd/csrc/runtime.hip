@@ -21,6 +21,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -670,31 +671,102 @@ cfm_status cfm_gemm_bf16(const void* A, int a_is_f32, int lda, const void* W, in
     return e == hipSuccess ? CFM_OK : fail(CFM_E_HIP, "launch failed: %s", hipGetErrorString(e));
 }
 
-cfm_status cfm_attention_bf16(const void* qk, const void* vt, const int32_t* kv_len,
-                              const uint8_t* key_mask, int rows, int T, int H, void* scratch,
-                              size_t scratch_bytes, void* o, void* stream) {
-    if (rows < 0 || T < 0 || H <= 0) return fail(CFM_E_VALUE, "bad rows/T/H");
-    if (rows > 65535 || H > 65535) return fail(CFM_E_SHAPE, "rows and H must be <= 65535");
-    if (rows == 0 || T == 0) return CFM_OK;
-    if (qk == nullptr || vt == nullptr || kv_len == nullptr || o == nullptr || scratch == nullptr)
-        return fail(CFM_E_NULL, "qk, vt, kv_len, scratch or o is NULL");
-    if (!aligned16(qk) || !aligned16(vt) || ((uintptr_t)o & 7) || ((uintptr_t)scratch & 15))
-        return fail(CFM_E_SHAPE, "qk, vt, scratch 16-byte / o 8-byte alignment");
+namespace {
+// bytes of key-validity tables the attention of `rows` rows of T keys needs: key
+// lengths, then (from the next 16-byte boundary, which the 64 bytes of slack
+// cover) per-key validity bytes and per-64-key-tile flags
+size_t attention_scratch_bytes(int rows, int T) {
     const long long Tp = round64(T);
-    const size_t need = (size_t)rows * 4 + (size_t)rows * Tp + (size_t)rows * (Tp / 64) + 64;
-    if (scratch_bytes < need) return fail(CFM_E_WORKSPACE, "scratch %zu bytes, need %zu", scratch_bytes, need);
-    int32_t* kvl = (int32_t*)scratch;
-    uint8_t* kvalid = (uint8_t*)scratch + align_up((size_t)rows * 4, 16);
+    return (size_t)rows * 4 + (size_t)rows * Tp + (size_t)rows * (Tp / 64) + 64;
+}
+
+// key tables + attention over caller-checked arguments, the tables in device memory `tables`
+cfm_status attention_bf16_run(const void* qk, const void* vt, const int32_t* kv_len, const uint8_t* key_mask,
+                              int rows, int T, int H, void* tables, void* o, hipStream_t s) {
+    const long long Tp = round64(T);
+    int32_t* kvl = (int32_t*)tables;
+    uint8_t* kvalid = (uint8_t*)tables + align_up((size_t)rows * 4, 16);
     uint8_t* tfull = kvalid + (size_t)rows * Tp;
     AttnParams p;
     p.qkv = qk; p.vt = vt; p.Tp = (int)Tp; p.o = o; p.rows = rows; p.T = T; p.H = H; p.hd = 64;
     p.kv_len = kvl; p.kv_mod = rows; p.key_mask = key_mask; p.mask_stride = T; p.P = 0;
     p.kvalid = kvalid; p.tile_full = tfull;
     (void)hipGetLastError();
-    launch_key_prep(key_mask, T, kv_len, rows, 0, T, (int)Tp, kvl, kvalid, tfull, (hipStream_t)stream);
-    launch_attention_bf16(p, (hipStream_t)stream);
+    launch_key_prep(key_mask, T, kv_len, rows, 0, T, (int)Tp, kvl, kvalid, tfull, s);
+    launch_attention_bf16(p, s);
     hipError_t e = hipGetLastError();
     return e == hipSuccess ? CFM_OK : fail(CFM_E_HIP, "launch failed: %s", hipGetErrorString(e));
+}
+
+cfm_status attention_bf16_check(const void* qk, const void* vt, const int32_t* kv_len, int rows, int T, int H,
+                                const void* o) {
+    if (rows < 0 || T < 0 || H <= 0) return fail(CFM_E_VALUE, "bad rows/T/H");
+    if (rows > 65535 || H > 65535) return fail(CFM_E_SHAPE, "rows and H must be <= 65535");
+    if (rows == 0 || T == 0) return CFM_OK;
+    if (qk == nullptr || vt == nullptr || kv_len == nullptr || o == nullptr)
+        return fail(CFM_E_NULL, "qk, vt, kv_len or o is NULL");
+    if (!aligned16(qk) || !aligned16(vt) || ((uintptr_t)o & 7))
+        return fail(CFM_E_SHAPE, "qk, vt 16-byte / o 8-byte alignment");
+    if (!attention_bf16_fits(T)) return fail(CFM_E_UNSUPPORTED, "T = %d: the key tables exceed LDS", T);
+    return CFM_OK;
+}
+
+constexpr size_t kNoAllocScratchBytes = (size_t)8 << 20;
+}  // namespace
+
+// Scratch of cfm_attention_bf16_noalloc (key-validity tables): one copy per GPU,
+// held until the process ends. Host code never passes `scratch` itself (on the
+// host the name is only a stand-in for the symbol); it passes the device address
+// that hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up once per device.
+cfm_status scratch_on_current_device(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(CFM_E_HIP, "hipGetDevice failed");
+    if (dev < 0 || dev >= kMaxDevices) return fail(CFM_E_UNSUPPORTED, "device index %d", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr)
+            return fail(CFM_E_HIP, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return CFM_OK;
+}
+}  // namespace
+
+cfm_status cfm_attention_bf16(const void* qk, const void* vt, const int32_t* kv_len,
+                              const uint8_t* key_mask, int rows, int T, int H, void* scratch_buf,
+                              size_t scratch_bytes, void* o, void* stream) {
+    cfm_status st = attention_bf16_check(qk, vt, kv_len, rows, T, H, o);
+    if (st != CFM_OK || rows == 0 || T == 0) return st;
+    if (scratch_buf == nullptr) return fail(CFM_E_NULL, "scratch is NULL");
+    if ((uintptr_t)scratch_buf & 15) return fail(CFM_E_SHAPE, "scratch must be 16-byte aligned");
+    const size_t need = attention_scratch_bytes(rows, T);
+    if (scratch_bytes < need) return fail(CFM_E_WORKSPACE, "scratch %zu bytes, need %zu", scratch_bytes, need);
+    return attention_bf16_run(qk, vt, kv_len, key_mask, rows, T, H, scratch_buf, o, (hipStream_t)stream);
+}
+
+cfm_status cfm_attention_bf16_noalloc(const void* qk, const void* vt, const int32_t* kv_len,
+                                      const uint8_t* key_mask, int rows, int T, int H, void* o, void* stream) {
+    cfm_status st = attention_bf16_check(qk, vt, kv_len, rows, T, H, o);
+    if (st != CFM_OK || rows == 0 || T == 0) return st;
+    const size_t need = attention_scratch_bytes(rows, T);
+    if (need > kNoAllocScratchBytes)
+        return fail(CFM_E_CAPACITY, "rows = %d, T = %d need %zu bytes of key tables; the built-in scratch holds %zu",
+                    rows, T, need, kNoAllocScratchBytes);
+    void* p = nullptr;
+    st = scratch_on_current_device(&p);
+    if (st != CFM_OK) return st;
+    return attention_bf16_run(qk, vt, kv_len, key_mask, rows, T, H, p, o, (hipStream_t)stream);
 }
 
 cfm_status cfm_adaln(const float* hsrc, const float* shift, const float* scale, int M, int d,

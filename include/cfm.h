@@ -237,6 +237,23 @@ cfm_status cfm_attention_bf16(const void* qk, const void* vt, const int32_t* kv_
                               const uint8_t* key_mask, int rows, int T, int H, void* scratch,
                               size_t scratch_bytes, void* o, void* stream);
 
+/* The same attention for callers that cannot allocate device memory or pass a
+ * workspace (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the key-validity tables live in a buffer built into the
+ * library, one 8 MiB copy per GPU held until the process ends, so this call
+ * allocates nothing. Arguments as cfm_attention_bf16 without scratch; rows * 4
+ * + rows * Tp + rows * Tp / 64 + 64 (the scratch size cfm_attention_bf16 asks for)
+ * must not exceed 8 MiB
+ * (CFM_E_CAPACITY otherwise; e.g. 128 rows of up to 64 000 keys). Every call on a
+ * GPU uses that GPU's one buffer: calls that overlap in time on one GPU (on
+ * different streams, or from different threads) race and must be serialised by
+ * the caller. Nothing in the buffer needs clearing: each call writes every table
+ * entry it reads. Errors as cfm_attention_bf16, plus CFM_E_HIP if the buffer's
+ * device address cannot be looked up. */
+cfm_status cfm_attention_bf16_noalloc(const void* qk, const void* vt, const int32_t* kv_len,
+                                      const uint8_t* key_mask, int rows, int T, int H, void* o,
+                                      void* stream);
+
 /* adaLN-modulated LayerNorm: y = LN(h) * (1 + scale) + shift, eps 1e-6, biased
  * variance, stats in fp32. h device fp32 [M, d]; shift, scale device fp32 [d];
  * y device bf16 (out_bf16 = 1) or fp32 [M, d]. d % 4 == 0. */
