@@ -23,7 +23,7 @@ KERNEL_CLASSES = {"gemm_qkv": 0, "gemm_proj": 1, "gemm_fc1": 2, "gemm_fc2": 3, "
                   "adaln": 5, "cfg_euler": 6, "gemm_in": 7, "gemm_out": 8, "hoisted": 9}
 
 EXPORTS = ["cfm_weights_bytes", "cfm_workspace_bytes", "cfm_weight_manifest", "cfm_create",
-           "cfm_sample", "cfm_destroy", "cfm_status_string", "cfm_last_error_detail",
+           "cfm_sample", "cfm_sample_ex", "cfm_destroy", "cfm_status_string", "cfm_last_error_detail",
            "cfm_profile_enable", "cfm_profile_read", "cfm_profile_disable", "cfm_cfg_euler",
            "cfm_gemm_bf16", "cfm_attention_bf16", "cfm_attention_bf16_noalloc", "cfm_adaln"]
 
@@ -39,6 +39,18 @@ class cfm_tensor_desc(C.Structure):
     _fields_ = [("name", C.c_char * 48), ("row0", C.c_int64), ("col0", C.c_int64),
                 ("rows", C.c_int64), ("cols", C.c_int64), ("ld", C.c_int64),
                 ("offset", C.c_int64), ("dtype", C.c_int32), ("reserved", C.c_int32)]
+
+
+SCHEDULES = {"uniform": 0, "quadratic": 1, "trailing": 2, "native": 3}
+SOLVERS = {"euler": 0, "midpoint": 1}
+GUIDANCE_MODES = {"full": 0, "interval": 1, "adaptive": 2}
+
+
+class cfm_sample_options(C.Structure):
+    _fields_ = [("schedule", C.c_int32), ("native_steps", C.c_int32), ("solver", C.c_int32),
+                ("guidance_mode", C.c_int32), ("interval_start", C.c_float), ("interval_end", C.c_float),
+                ("adaptive_threshold", C.c_float), ("adaptive_warmup", C.c_int32),
+                ("adaptive_patience", C.c_int32), ("reserved", C.c_int32), ("guided_evals", C.c_void_p)]
 
 
 class CfmError(RuntimeError):
@@ -71,6 +83,8 @@ def load() -> C.CDLL:
     lib.cfm_create.restype = i32
     lib.cfm_sample.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, f32p, vp, vp]
     lib.cfm_sample.restype = i32
+    lib.cfm_sample_ex.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, f32p, C.POINTER(cfm_sample_options), vp, vp]
+    lib.cfm_sample_ex.restype = i32
     lib.cfm_destroy.argtypes = [vp]
     lib.cfm_destroy.restype = None
     lib.cfm_status_string.argtypes = [i32]
@@ -272,19 +286,37 @@ class Sampler:
             pass
 
     def sample(self, x0, cond, *, mask=None, spk=None, n_steps: int, guidance: Sequence[float] = (),
-               out=None, stream=None):
-        """out[R, Tx, C] (fp32, device) after n_steps Euler steps; out may be x0 itself."""
+               out=None, stream=None, schedule: str = "uniform", native_steps: Optional[int] = None,
+               solver: str = "euler", guidance_mode: str = "full", interval=(0.0, 1.0),
+               adaptive=(0.015, 4, 2), guided_evals=None):
+        """out[R, Tx, C] (fp32, device) after n_steps solver steps; out may be x0 itself.
+
+        schedule / native_steps / solver / guidance_mode / interval / adaptive
+        (threshold, warmup, patience) select the sampler-level options of
+        cfm_sample_ex; guided_evals, an int32 [R] device tensor, receives per request
+        the number of evaluations that ran its unconditional rows."""
         import torch
         guidance = tuple(guidance)
-        check_sample_args(self.cfg, x0, cond, mask, spk, out, n_steps, guidance)
+        evals = int(n_steps) * (2 if solver == "midpoint" else 1)
+        check_sample_args(self.cfg, x0, cond, mask, spk, out, evals, guidance)
         if x0.device != self.weights.device:
             raise ValueError(f"inputs on {x0.device}, sampler on {self.weights.device}")
         R, Tx = int(x0.shape[0]), int(x0.shape[1])
+        if guided_evals is not None:
+            _need("guided_evals", guided_evals, (R,), torch.int32)
+            _on_device(x0=x0, guided_evals=guided_evals)
+        for name, val, table in (("schedule", schedule, SCHEDULES), ("solver", solver, SOLVERS),
+                                 ("guidance_mode", guidance_mode, GUIDANCE_MODES)):
+            if val not in table:
+                raise ValueError(f"{name} {val!r} not one of {sorted(table)}")
         if out is None:
             out = torch.empty_like(x0)
         g = (C.c_float * max(1, len(guidance)))(*[float(v) for v in guidance])
-        check(load().cfm_sample(self._ctx, _ptr(x0), _ptr(cond), _ptr(spk), _ptr(mask), R, Tx,
-                                int(n_steps), g, _ptr(out), _stream(stream)))
+        opt = cfm_sample_options(SCHEDULES[schedule], int(native_steps or 0), SOLVERS[solver],
+                                 GUIDANCE_MODES[guidance_mode], float(interval[0]), float(interval[1]),
+                                 float(adaptive[0]), int(adaptive[1]), int(adaptive[2]), 0, _ptr(guided_evals))
+        check(load().cfm_sample_ex(self._ctx, _ptr(x0), _ptr(cond), _ptr(spk), _ptr(mask), R, Tx,
+                                   int(n_steps), g, C.byref(opt), _ptr(out), _stream(stream)))
         return out
 
     def profile_enable(self, kernel_class: str, capacity: int):

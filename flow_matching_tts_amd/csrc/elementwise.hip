@@ -12,40 +12,98 @@ namespace {
 // Fused CFG combine + Euler update (VoiceHub "Diffusion and flow TTS
 // optimization", section "Custom Triton and CUDA kernels", names the guidance
 // combine fused with the Euler step as a kernel worth writing):
-// x += sum_b (dt * w_b) * v_b, read once, written once; masked frames are
-// neither read nor written. Each thread owns EU float4s of x spaced one grid
-// apart (coalesced per instruction) and issues all of their loads before any
-// arithmetic. One float4 per thread measured fastest (more per thread gives
-// fewer, longer-lived waves and no gain in bytes in flight).
-constexpr int EU = 1;
-
+// x_out = x_in + sum_b (dt * w_b) * v_b, one float4 of x per thread, read once,
+// written once. The loads of x and of every branch's velocity are issued before
+// the frame's mask byte is looked at (all are in range whatever the mask), so the
+// mask does not put a second dependent round trip in front of them. Masked frames
+// are not written when the update is in place; with a separate output (the
+// midpoint solver's half step) they are copied, so the output is defined
+// everywhere. Requests whose unconditional lane is off (adaptive guidance) take
+// the fully conditioned branch alone: x_out = x_in + w_full * v_{nb-1}.
 __global__ void __launch_bounds__(256)
 cfg_euler_kernel(const f32x4* __restrict__ v, int nb, float w0, float w1, float w2,
-                 const uint8_t* __restrict__ mask, long long n4, int c4, long long branch4,
-                 f32x4* __restrict__ x) {
-    const long long stride = (long long)gridDim.x * blockDim.x;
-    const long long i0 = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-    f32x4 xv[EU], a[EU], b[EU], c[EU];
-    bool ok[EU];
-#pragma unroll
-    for (int u = 0; u < EU; ++u) {
-        const long long i = i0 + u * stride;
-        ok[u] = i < n4 && (mask == nullptr || mask[i / c4] != 0);
-        if (ok[u]) {
-            xv[u] = *(x + i);
-            a[u] = *(v + i);
-            if (nb > 1) b[u] = *(v + branch4 + i);
-            if (nb > 2) c[u] = *(v + 2 * branch4 + i);
-        }
+                 const uint8_t* __restrict__ mask, long long n4, int c4, long long branch4, int Tx,
+                 const f32x4* x_in, f32x4* x_out, const int32_t* __restrict__ lane_off, float w_full) {
+    const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n4) return;
+    const f32x4 xv = x_in[i];
+    const f32x4 a = v[i];
+    f32x4 b = f32x4{}, c = f32x4{};
+    if (nb > 1) b = v[branch4 + i];
+    if (nb > 2) c = v[2 * branch4 + i];
+    const long long f = i / c4;                       // frame r * Tx + t
+    const bool ok = mask == nullptr || mask[f] != 0;
+    const bool off = lane_off != nullptr && lane_off[f / Tx] != 0;
+    if (!ok) {
+        if (x_out != x_in) x_out[i] = xv;
+        return;
     }
-#pragma unroll
-    for (int u = 0; u < EU; ++u) {
-        if (!ok[u]) continue;
-        f32x4 acc = xv[u] + w0 * a[u];
-        if (nb > 1) acc += w1 * b[u];
-        if (nb > 2) acc += w2 * c[u];
-        x[i0 + u * stride] = acc;
+    f32x4 acc;
+    if (off) {
+        acc = xv + w_full * (nb > 2 ? c : nb > 1 ? b : a);
+    } else {
+        acc = xv + w0 * a;
+        if (nb > 1) acc += w1 * b;
+        if (nb > 2) acc += w2 * c;
     }
+    x_out[i] = acc;
+}
+
+// Adaptive guidance, once per step after its first (left-endpoint) evaluation:
+// one block per request reduces, over the request's valid frames,
+// sum |v_full - v_u| and sum |v_full| (fixed order: per-thread strided sums,
+// then a tree in LDS), and advances the request's lane state from st_in to
+// st_out (state: count [R], off [R], guided evaluations [R]). Steps before
+// `warmup` never count; from then on a metric below the threshold increments
+// the count and any other resets it; the lane stops once the count reaches
+// `patience`. A stopped lane stays stopped.
+constexpr int AG_NT = 256;
+__global__ void __launch_bounds__(AG_NT)
+adaptive_update_kernel(const float* __restrict__ v, int nb, long long branch_stride, const uint8_t* __restrict__ mask,
+                       int Tx, int C, const int32_t* __restrict__ st_in, int32_t* __restrict__ st_out, int R,
+                       int step, int warmup, int patience, float threshold, int evals_per_step) {
+    __shared__ float sn[AG_NT], sd[AG_NT];
+    const int r = blockIdx.x, tid = threadIdx.x;
+    const int count = st_in[r], off = st_in[R + r], guided = st_in[2 * R + r];
+    if (off) {
+        if (tid == 0) { st_out[r] = count; st_out[R + r] = 1; st_out[2 * R + r] = guided; }
+        return;
+    }
+    const float* vu = v + (long long)r * Tx * C;
+    const float* vf = vu + (long long)(nb - 1) * branch_stride;
+    float num = 0.0f, den = 0.0f;
+    const long long n = (long long)Tx * C;
+    for (long long e = tid; e < n; e += AG_NT) {
+        if (mask != nullptr && mask[(long long)r * Tx + e / C] == 0) continue;
+        const float f = vf[e];
+        num += fabsf(f - vu[e]);
+        den += fabsf(f);
+    }
+    sn[tid] = num;
+    sd[tid] = den;
+    __syncthreads();
+    for (int o = AG_NT / 2; o > 0; o >>= 1) {
+        if (tid < o) { sn[tid] += sn[tid + o]; sd[tid] += sd[tid + o]; }
+        __syncthreads();
+    }
+    if (tid == 0) {
+        const float metric = sd[0] > 0.0f ? sn[0] / sd[0] : 0.0f;
+        int c2 = count;
+        if (step >= warmup) c2 = metric < threshold ? count + 1 : 0;
+        st_out[r] = c2;
+        st_out[R + r] = c2 >= patience ? 1 : 0;
+        st_out[2 * R + r] = guided + evals_per_step;
+    }
+}
+
+__global__ void fill_i32_kernel(int32_t* p, int n, int value) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = value;
+}
+
+__global__ void copy_i32_kernel(const int32_t* src, int32_t* dst, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) dst[i] = src[i];
 }
 
 // ---------------------------------------------------------------------------
@@ -144,18 +202,43 @@ adaln_kernel(LnParams p, int tpw) {
 }
 
 // ---------------------------------------------------------------------------
-// temb[k, i] = cos(1000 t_k w_i) for i < F/2, sin(1000 t_k w_(i-F/2)) otherwise,
-// w_i = 10000^(-i/(F/2)), t_k = k/S; phase computed in fp64.
-__global__ void timestep_embedding_kernel(float* temb, int S, int F) {
+// Time of evaluation j of a sampling call (fp64). Step k runs from t_k to t_k+1 on
+// the grid of S steps: u = k / S and t_k = u (uniform), u^2 (quadratic),
+// 1 - (1 - u)^2 (trailing), or n_k / N with n_k = round(k N / S), halves up, on a
+// native grid of N uniform steps. With one evaluation per step (Euler) evaluation
+// j is at t_j; with two (midpoint) evaluation 2k is at t_k and 2k + 1 at
+// t_k + (t_k+1 - t_k) / 2. The host computes the same times for the step sizes.
+__host__ __device__ inline double grid_time(int kind, int S, int N, int k) {
+    if (k <= 0) return 0.0;
+    if (k >= S) return 1.0;
+    const double u = (double)k / (double)S;
+    switch (kind) {
+        case 1: return u * u;
+        case 2: return 1.0 - (1.0 - u) * (1.0 - u);
+        case 3: return (double)((2LL * k * N + S) / (2LL * S)) / (double)N;
+        default: return u;
+    }
+}
+
+__host__ __device__ inline double eval_time(int kind, int S, int N, int per_step, int j) {
+    const int k = j / per_step;
+    const double t0 = grid_time(kind, S, N, k);
+    if (j % per_step == 0) return t0;
+    return t0 + 0.5 * (grid_time(kind, S, N, k + 1) - t0);
+}
+
+// temb[j, i] = cos(1000 t_j w_i) for i < F/2, sin(1000 t_j w_(i-F/2)) otherwise,
+// w_i = 10000^(-i/(F/2)), t_j the time of evaluation j; phase computed in fp64.
+__global__ void timestep_embedding_kernel(float* temb, int n_eval, int F, int kind, int S, int N, int per_step) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    const int k = blockIdx.y;
-    if (i >= F || k >= S) return;
+    const int j = blockIdx.y;
+    if (i >= F || j >= n_eval) return;
     const int half = F / 2;
     const int fi = i < half ? i : i - half;
-    const double t = (double)k / (double)S;
+    const double t = eval_time(kind, S, N, per_step, j);
     const double w = exp(-log(10000.0) * (double)fi / (double)half);
     const double arg = 1000.0 * t * w;
-    temb[(long long)k * F + i] = (float)(i < half ? cos(arg) : sin(arg));
+    temb[(long long)j * F + i] = (float)(i < half ? cos(arg) : sin(arg));
 }
 
 // Per-request key validity (see launch_key_prep). One block per request.
@@ -197,13 +280,22 @@ __global__ void key_prep_kernel(const uint8_t* mask, int mask_stride, const int3
 // are written out. Row i = b*R + r holds kv_len[r] tokens rounded up to a
 // multiple of 8, so that every row starts 8-token aligned.
 constexpr int PACK_NT = 256;
-__global__ void __launch_bounds__(PACK_NT) pack_offsets_kernel(const int32_t* kv_len, int R, int N, int32_t* row_off) {
+// With lane_off (adaptive guidance), the rows of every branch but the last of a
+// request whose unconditional lane is off hold no token.
+__device__ __forceinline__ int packed_len(const int32_t* kv_len, const int32_t* lane_off, int R, int nb, int i) {
+    const int r = i % R;
+    if (lane_off != nullptr && i / R < nb - 1 && lane_off[r] != 0) return 0;
+    return (kv_len[r] + 7) & ~7;
+}
+
+__global__ void __launch_bounds__(PACK_NT) pack_offsets_kernel(const int32_t* kv_len, const int32_t* lane_off, int R,
+                                                              int nb, int N, int32_t* row_off) {
     __shared__ int part[PACK_NT];
     const int tid = threadIdx.x;
     const int per = (N + PACK_NT - 1) / PACK_NT;
     const int lo = min(N, tid * per), hi = min(N, lo + per);
     int sum = 0;
-    for (int i = lo; i < hi; ++i) sum += (kv_len[i % R] + 7) & ~7;
+    for (int i = lo; i < hi; ++i) sum += packed_len(kv_len, lane_off, R, nb, i);
     part[tid] = sum;
     __syncthreads();
     for (int o = 1; o < PACK_NT; o <<= 1) {
@@ -215,7 +307,7 @@ __global__ void __launch_bounds__(PACK_NT) pack_offsets_kernel(const int32_t* kv
     int run = part[tid] - sum;   // exclusive prefix of this thread's run
     for (int i = lo; i < hi; ++i) {
         row_off[i] = run;
-        run += (kv_len[i % R] + 7) & ~7;
+        run += packed_len(kv_len, lane_off, R, nb, i);
     }
     if (tid == PACK_NT - 1) row_off[N] = part[tid];
 }
@@ -257,14 +349,32 @@ __global__ void prefix_init_kernel(const float* cproj, const float* bias, int R,
 
 }  // namespace
 
-void launch_cfg_euler(const float* v, int nb, float w0, float w1, float w2, const uint8_t* mask,
-                      int R, int Tx, int C, float* x, hipStream_t s) {
-    const long long n4 = (long long)R * Tx * C / 4;
+void launch_cfg_euler(const CfgEulerArgs& a, hipStream_t s) {
+    const long long n4 = (long long)a.R * a.Tx * a.C / 4;
     if (n4 <= 0) return;
-    const int blocks = (int)((n4 + 256LL * EU - 1) / (256LL * EU));
-    cfg_euler_kernel<<<blocks, 256, 0, s>>>((const f32x4*)v, nb, w0, w1, w2, mask, n4, C / 4, n4,
-                                             (f32x4*)x);
+    const int blocks = (int)((n4 + 255) / 256);
+    cfg_euler_kernel<<<blocks, 256, 0, s>>>((const f32x4*)a.v, a.nb, a.w0, a.w1, a.w2, a.mask, n4, a.C / 4, n4, a.Tx,
+                                             (const f32x4*)a.x_in, (f32x4*)a.x_out, a.lane_off, a.w_full);
 }
+
+void launch_adaptive_update(const float* v, int nb, const uint8_t* mask, int R, int Tx, int C, const int32_t* st_in,
+                            int32_t* st_out, int step, int warmup, int patience, float threshold, int evals_per_step,
+                            hipStream_t s) {
+    if (R <= 0) return;
+    adaptive_update_kernel<<<R, AG_NT, 0, s>>>(v, nb, (long long)R * Tx * C, mask, Tx, C, st_in, st_out, R, step,
+                                               warmup, patience, threshold, evals_per_step);
+}
+
+void launch_fill_i32(int32_t* p, int n, int value, hipStream_t s) {
+    if (n > 0) fill_i32_kernel<<<(n + 255) / 256, 256, 0, s>>>(p, n, value);
+}
+
+void launch_copy_i32(const int32_t* src, int32_t* dst, int n, hipStream_t s) {
+    if (n > 0) copy_i32_kernel<<<(n + 255) / 256, 256, 0, s>>>(src, dst, n);
+}
+
+double host_eval_time(int kind, int S, int N, int per_step, int j) { return eval_time(kind, S, N, per_step, j); }
+double host_grid_time(int kind, int S, int N, int k) { return grid_time(kind, S, N, k); }
 
 template <int V>
 void launch_adaln_v(const LnParams& p, hipStream_t s) {
@@ -285,9 +395,9 @@ void launch_adaln(const LnParams& p, hipStream_t s) {
     else launch_adaln_v<16>(p, s);
 }
 
-void launch_timestep_embedding(float* temb, int S, int F, hipStream_t s) {
-    if (S <= 0) return;
-    timestep_embedding_kernel<<<dim3((F + 127) / 128, S), 128, 0, s>>>(temb, S, F);
+void launch_timestep_embedding(float* temb, int n_eval, int F, int kind, int S, int N, int per_step, hipStream_t s) {
+    if (n_eval <= 0) return;
+    timestep_embedding_kernel<<<dim3((F + 127) / 128, n_eval), 128, 0, s>>>(temb, n_eval, F, kind, S, N, per_step);
 }
 
 void launch_key_prep(const uint8_t* mask, int mask_stride, const int32_t* kv_len_in, int R, int P,
@@ -297,11 +407,11 @@ void launch_key_prep(const uint8_t* mask, int mask_stride, const int32_t* kv_len
     key_prep_kernel<<<R, 256, 0, s>>>(mask, mask_stride, kv_len_in, P, T, Tp, kv_len_out, kvalid, tile_full);
 }
 
-void launch_pack_rows(const int32_t* kv_len, int R, int nb, int NTmax, int32_t* row_off, int32_t* tok_row,
-                      hipStream_t s) {
+void launch_pack_rows(const int32_t* kv_len, const int32_t* lane_off, int R, int nb, int NTmax, int32_t* row_off,
+                      int32_t* tok_row, hipStream_t s) {
     const int N = nb * R;
     if (N <= 0) return;
-    pack_offsets_kernel<<<1, PACK_NT, 0, s>>>(kv_len, R, N, row_off);
+    pack_offsets_kernel<<<1, PACK_NT, 0, s>>>(kv_len, lane_off, R, nb, N, row_off);
     if (NTmax > 0) pack_rows_kernel<<<(NTmax + 255) / 256, 256, 0, s>>>(row_off, N, NTmax, tok_row);
 }
 

@@ -63,6 +63,9 @@ __device__ __forceinline__ void epi_store(const EpiParams& p, int m, int n, floa
 template <int EPI>
 __device__ __forceinline__ void epi_store_vec4(const EpiParams& p, int m, int n, f32x4 v,
                                                const f32x4* bias4 = nullptr) {
+    // the in-projection's conditioned branches add the condition term (which holds
+    // the bias) to the bare accumulator, as every other in-projection path does
+    const f32x4 acc = v;
     if (bias4) v += *bias4;                        // preloaded by the caller (same columns)
     else if (p.bias) v += *(const f32x4*)(p.bias + n);
     if constexpr (EPI == EPI_F32) {
@@ -79,10 +82,8 @@ __device__ __forceinline__ void epi_store_vec4(const EpiParams& p, int m, int n,
         *h += *(const f32x4*)(p.gate.at((long long)m) + n) * v;
     } else if constexpr (EPI == EPI_INPROJ) {
         const int r = m / p.Tx, t = m - r * p.Tx;
-        // v already holds acc + bias; the conditioned branches use acc + cproj instead
-        const f32x4 withc = p.cproj ? v - (p.bias ? *(const f32x4*)(p.bias + n) : f32x4{}) +
-                                          *(const f32x4*)(p.cproj + (long long)m * p.ldo + n)
-                                    : v;
+        // v holds acc + bias; the conditioned branches use acc + cproj instead
+        const f32x4 withc = p.cproj ? acc + *(const f32x4*)(p.cproj + (long long)m * p.ldo + n) : v;
         for (int br = 0; br < p.nb; ++br) {
             long long tok;
             if (p.row_off) {
@@ -285,29 +286,43 @@ __device__ __forceinline__ void epi_tile_gated(const EpiParams& p, const f32x16 
         }
         return;
     }
-    auto fetch = [&](int b, f32x4 (&hv)[4], f32x4 (&gv)[4]) {
+    // Per-row gate vectors (a speaker branch: its rows read their request's own
+    // modulation). Tokens are laid out row after row, so the 32 tokens of a block
+    // nearly always belong to one row: the gate pointers of a block's first and
+    // last token are compared (wave-uniform), and when they are equal every token
+    // of the block reads that one vector (rows are monotone in the token index and
+    // the speaker branch is the last branch, so equal pointers mean one row, or
+    // only rows that share vector 0). Such a block's gate is read ahead with its
+    // residual, one 16-byte load per lane; a block that straddles rows with
+    // different vectors looks its gates up per row when it is stored.
+    const float* gbase[TM];
+    bool guni[TM];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const long long mf = mb0 + i * 32, ml = min(mf + 31, (long long)M - 1);
+        gbase[i] = mf < M ? p.gate.at(mf) : p.gate.base;
+        guni[i] = mf >= M || gbase[i] == p.gate.at(ml);
+    }
+    constexpr int AH = 3;
+    f32x4 hq[AH + 1][4], gq[AH + 1];
+    auto fetch = [&](int b, f32x4 (&hv)[4], f32x4& gv) {
         const int i = b / TN, j = b % TN;
         const int n = nb0 + j * 32 + c0;
+        gv = guni[i] ? *(const f32x4*)(gbase[i] + n) : f32x4{};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int m = mb0 + i * 32 + (lane >> 3) + 8 * q;
-            const bool ok = m < M;
-            hv[q] = ok ? *(const f32x4*)((const float*)p.out + (long long)m * p.ldo + n) : f32x4{};
-            gv[q] = ok ? *(const f32x4*)(p.gate.at((long long)m) + n) : f32x4{};
+            hv[q] = m < M ? *(const f32x4*)((const float*)p.out + (long long)m * p.ldo + n) : f32x4{};
         }
     };
-    // blocks whose h and gate loads are in flight: one (2 x 16 VGPRs per block;
-    // two spill beside the 128 accumulator VGPRs)
-    constexpr int AHEAD = 1;
-    f32x4 hq[AHEAD + 1][4], gq[AHEAD + 1][4];
 #pragma unroll
-    for (int b = 0; b < AHEAD && b < TM * TN; ++b) fetch(b, hq[b], gq[b]);
+    for (int b = 0; b < AH && b < TM * TN; ++b) fetch(b, hq[b], gq[b]);
 #pragma unroll
     for (int b = 0; b < TM * TN; ++b) {
         const int i = b / TN, j = b % TN;
-        if (b + AHEAD < TM * TN) fetch(b + AHEAD, hq[(b + AHEAD) % (AHEAD + 1)], gq[(b + AHEAD) % (AHEAD + 1)]);
-        const f32x4 (&hcur)[4] = hq[b % (AHEAD + 1)];
-        const f32x4 (&gcur)[4] = gq[b % (AHEAD + 1)];
+        if (b + AH < TM * TN) fetch(b + AH, hq[(b + AH) % (AH + 1)], gq[(b + AH) % (AH + 1)]);
+        const f32x4 (&hcur)[4] = hq[b % (AH + 1)];
+        const f32x4 gcur = gq[b % (AH + 1)];
         const int mb = mb0 + i * 32, n = nb0 + j * 32 + c0;
         const int li = lane & 31, lh = lane >> 5;
 #pragma unroll
@@ -321,7 +336,8 @@ __device__ __forceinline__ void epi_tile_gated(const EpiParams& p, const f32x16 
             const int m = mb + row;
             if (m >= M) continue;
             const f32x4 v = *(const f32x4*)(wl + row * EPI_RP + c0) + bias[j];
-            *(f32x4*)((float*)p.out + (long long)m * p.ldo + n) = hcur[q] + gcur[q] * v;
+            const f32x4 g = guni[i] ? gcur : *(const f32x4*)(p.gate.at((long long)m) + n);
+            *(f32x4*)((float*)p.out + (long long)m * p.ldo + n) = hcur[q] + g * v;
         }
         __builtin_amdgcn_wave_barrier();
     }

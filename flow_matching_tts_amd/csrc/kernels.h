@@ -91,10 +91,34 @@ struct LnParams {
 };
 void launch_adaln(const LnParams& p, hipStream_t s);
 
-void launch_cfg_euler(const float* v, int nb, float w0, float w1, float w2, const uint8_t* mask,
-                      int R, int Tx, int C, float* x, hipStream_t s);
-// temb [S, F] = sinusoidal embedding of t_k = k / S (phase in fp64)
-void launch_timestep_embedding(float* temb, int S, int F, hipStream_t s);
+// x_out = x_in + sum_b w_b v_b on valid frames (v [nb, R, Tx, C]); masked frames are
+// left alone in place, copied when x_out != x_in; requests with lane_off[r] != 0 take
+// x_in + w_full v_{nb-1}.
+struct CfgEulerArgs {
+    const float* v = nullptr;
+    int nb = 1;
+    float w0 = 0.0f, w1 = 0.0f, w2 = 0.0f;
+    const uint8_t* mask = nullptr;
+    int R = 0, Tx = 0, C = 0;
+    const float* x_in = nullptr;
+    float* x_out = nullptr;
+    const int32_t* lane_off = nullptr;
+    float w_full = 0.0f;
+};
+void launch_cfg_euler(const CfgEulerArgs& a, hipStream_t s);
+// adaptive guidance state update after a step's first evaluation (state [count R | off R | guided R])
+void launch_adaptive_update(const float* v, int nb, const uint8_t* mask, int R, int Tx, int C, const int32_t* st_in,
+                            int32_t* st_out, int step, int warmup, int patience, float threshold, int evals_per_step,
+                            hipStream_t s);
+void launch_fill_i32(int32_t* p, int n, int value, hipStream_t s);
+void launch_copy_i32(const int32_t* src, int32_t* dst, int n, hipStream_t s);
+// Evaluation times of a sampling call: grid kind 0 uniform, 1 quadratic, 2 trailing,
+// 3 native subsequence of N uniform steps; per_step evaluations per step (1 Euler,
+// 2 midpoint). The host and the timestep-embedding kernel use the same function.
+double host_grid_time(int kind, int S, int N, int k);
+double host_eval_time(int kind, int S, int N, int per_step, int j);
+// temb [n_eval, F] = sinusoidal embedding of every evaluation time (phase in fp64)
+void launch_timestep_embedding(float* temb, int n_eval, int F, int kind, int S, int N, int per_step, hipStream_t s);
 // Key validity of every request's sequence (P prefix keys, then Tx = T - P frames):
 // kv_len_out[r] = min(kv_len_in[r], T) if kv_len_in is given, else P + 1 + the
 // index of the last valid frame (P if none); kvalid[r, t] = t < kv_len_out[r] and
@@ -104,11 +128,12 @@ void launch_key_prep(const uint8_t* mask, int mask_stride, const int32_t* kv_len
                      int T, int Tp, int32_t* kv_len_out, uint8_t* kvalid, uint8_t* tile_full,
                      hipStream_t s);
 // Packed row layout of a variable-length batch: rows are branch-major (row =
-// b*R + r) and row i holds kv_len[r] tokens rounded up to a multiple of 8;
-// row_off[N + 1] prefix offsets (row_off[N] = total tokens) and tok_row[t] = row
-// of packed token t (-1 past the end, up to NTmax).
-void launch_pack_rows(const int32_t* kv_len, int R, int nb, int NTmax, int32_t* row_off, int32_t* tok_row,
-                      hipStream_t s);
+// b*R + r) and row i holds kv_len[r] tokens rounded up to a multiple of 8 (none
+// when b < nb - 1 and lane_off[r] != 0, lane_off optional); row_off[N + 1] prefix
+// offsets (row_off[N] = total tokens) and tok_row[t] = row of packed token t (-1
+// past the end, up to NTmax).
+void launch_pack_rows(const int32_t* kv_len, const int32_t* lane_off, int R, int nb, int NTmax, int32_t* row_off,
+                      int32_t* tok_row, hipStream_t s);
 // cvec[(k*nc + ci), :] = ct[k, :] + (spk ? (ci == 0 ? bs : spkproj[ci-1]) : 0)
 void launch_assemble_cvec(const float* ct, const float* bs, const float* spkproj, int S, int nc,
                           int d, float* cvec, hipStream_t s);

@@ -187,7 +187,7 @@ Slot find(const Manifest& m, const char* name, long long col0 = 0) {
 
 struct Layout {   // workspace regions, byte offsets
     size_t h, act, big, vt, v, cproj, temb, tpre, ct, spkproj, cvec, mod, kvlen, kvalid, tfull, rowoff, tokrow,
-        total;
+        xmid, lanes, total;
 };
 
 inline long long round64(long long v) { return (v + 63) / 64 * 64; }
@@ -226,6 +226,8 @@ Layout plan_workspace(const cfm_config& c) {
     L.tfull = take(Rm * (size_t)round64(T) / 64);       // per-64-key-tile "all valid" bytes
     L.rowoff = take(packable ? (N + 1) * 4 : 0);
     L.tokrow = take(packable ? N * TT * 4 : 0);
+    L.xmid = take(Rm * Tx * c.latent_dim * 4);          // midpoint solver: x at the half step
+    L.lanes = take(2 * 3 * Rm * 4);                      // adaptive guidance: two states [count | off | guided]
     L.total = off;
     return L;
 }
@@ -410,15 +412,72 @@ cfm_status cfm_profile_disable(cfm_ctx* c) {
     return CFM_OK;
 }
 
+namespace {
+
+struct Opts {                  // validated cfm_sample_options
+    int schedule = CFM_SCHEDULE_UNIFORM, native = 0, solver = CFM_SOLVER_EULER, mode = CFM_GUIDANCE_FULL;
+    double start = 0.0, end = 1.0;
+    float threshold = 0.0f;
+    int warmup = 0, patience = 1;
+    int32_t* guided_out = nullptr;
+};
+
+cfm_status read_options(const cfm_sample_options* o, int S, Opts& out) {
+    out = Opts{};
+    if (o == nullptr) return CFM_OK;
+    if (o->schedule < CFM_SCHEDULE_UNIFORM || o->schedule > CFM_SCHEDULE_NATIVE)
+        return fail(CFM_E_VALUE, "schedule %d", o->schedule);
+    if (o->solver != CFM_SOLVER_EULER && o->solver != CFM_SOLVER_MIDPOINT) return fail(CFM_E_VALUE, "solver %d", o->solver);
+    if (o->guidance_mode < CFM_GUIDANCE_FULL || o->guidance_mode > CFM_GUIDANCE_ADAPTIVE)
+        return fail(CFM_E_VALUE, "guidance_mode %d", o->guidance_mode);
+    if (o->schedule == CFM_SCHEDULE_NATIVE && (o->native_steps < S || o->native_steps <= 0))
+        return fail(CFM_E_VALUE, "native schedule: native_steps %d must be >= n_steps %d and > 0", o->native_steps, S);
+    if (o->guidance_mode == CFM_GUIDANCE_INTERVAL && (!std::isfinite(o->interval_start) || !std::isfinite(o->interval_end)))
+        return fail(CFM_E_VALUE, "guidance interval must be finite");
+    if (o->guidance_mode == CFM_GUIDANCE_ADAPTIVE) {
+        if (std::isnan(o->adaptive_threshold) || o->adaptive_threshold < 0.0f)
+            return fail(CFM_E_VALUE, "adaptive threshold must be >= 0 (infinity allowed)");
+        if (o->adaptive_warmup < 0 || o->adaptive_patience < 1)
+            return fail(CFM_E_VALUE, "adaptive warmup must be >= 0 and patience >= 1");
+    }
+    out.schedule = o->schedule;
+    out.native = o->native_steps;
+    out.solver = o->solver;
+    out.mode = o->guidance_mode;
+    out.start = o->interval_start;
+    out.end = o->interval_end;
+    out.threshold = o->adaptive_threshold;
+    out.warmup = o->adaptive_warmup;
+    out.patience = o->adaptive_patience;
+    out.guided_out = o->guided_evals;
+    return CFM_OK;
+}
+
+}  // namespace
+
 cfm_status cfm_sample(cfm_ctx* c, const float* x0, const float* cond, const float* spk,
                       const uint8_t* frame_mask, int R, int Tx, int S,
                       const float* guidance, float* out, void* stream) {
+    return cfm_sample_ex(c, x0, cond, spk, frame_mask, R, Tx, S, guidance, nullptr, out, stream);
+}
+
+cfm_status cfm_sample_ex(cfm_ctx* c, const float* x0, const float* cond, const float* spk,
+                         const uint8_t* frame_mask, int R, int Tx, int S, const float* guidance,
+                         const cfm_sample_options* options, float* out, void* stream) {
     if (c == nullptr) return fail(CFM_E_NULL, "ctx is NULL");
     const cfm_config& g = c->cfg;
     if (R < 0 || Tx < 0 || S < 0) return fail(CFM_E_VALUE, "negative n_requests, n_frames or n_steps");
-    if (R > g.max_requests || Tx > g.max_frames || S > g.max_steps)
-        return fail(CFM_E_CAPACITY, "R=%d Tx=%d S=%d above capacity %d/%d/%d", R, Tx, S,
+    Opts op;
+    {
+        cfm_status st = read_options(options, S, op);
+        if (st != CFM_OK) return st;
+    }
+    const int per_step = op.solver == CFM_SOLVER_MIDPOINT ? 2 : 1;
+    const long long n_eval_ll = (long long)S * per_step;
+    if (R > g.max_requests || Tx > g.max_frames || n_eval_ll > g.max_steps)
+        return fail(CFM_E_CAPACITY, "R=%d Tx=%d evaluations=%lld above capacity %d/%d/%d", R, Tx, n_eval_ll,
                     g.max_requests, g.max_frames, g.max_steps);
+    const int n_eval = (int)n_eval_ll;
     const int nb = g.n_branches;
     if (nb > 1 && guidance == nullptr) return fail(CFM_E_NULL, "guidance is NULL");
     float scales[2] = {0.0f, 0.0f};
@@ -431,6 +490,8 @@ cfm_status cfm_sample(cfm_ctx* c, const float* x0, const float* cond, const floa
     if (g.spk_dim > 0 && spk == nullptr) return fail(CFM_E_NULL, "spk is NULL");
     if (!aligned16(x0) || !aligned16(out) || !aligned16(cond) || (spk && !aligned16(spk)))
         return fail(CFM_E_SHAPE, "x0, cond, spk and out must be 16-byte aligned");
+    if (op.guided_out != nullptr && ((uintptr_t)op.guided_out & 3))
+        return fail(CFM_E_SHAPE, "guided_evals must be 4-byte aligned");
     const int C = g.latent_dim, d = g.d_model, L = g.n_layers;
     const size_t xbytes = (size_t)R * Tx * C * sizeof(float);
     {
@@ -443,19 +504,22 @@ cfm_status cfm_sample(cfm_ctx* c, const float* x0, const float* cond, const floa
     (void)hipGetLastError();   // clear a stale error of an earlier, unrelated call
     if (out != x0 && hipMemcpyAsync(out, x0, xbytes, hipMemcpyDeviceToDevice, s) != hipSuccess)
         return fail(CFM_E_HIP, "hipMemcpyAsync failed");
-    if (S == 0) return CFM_OK;
+    int32_t* lanes = wsp<int32_t>(c, c->lay.lanes);   // two adaptive states of 3R ints
+    if (S == 0) {
+        if (op.guided_out) launch_fill_i32(op.guided_out, R, 0, s);
+        hipError_t e = hipGetLastError();
+        return e == hipSuccess ? CFM_OK : fail(CFM_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    }
 
     const bool bf = g.dtype == CFM_BF16;
     const bool prefix = g.cond_mode == CFM_COND_PREFIX;
     const int P = prefix ? g.n_prefix : 0;
     const int T = Tx + P, N = nb * R;
-    const long long NT = (long long)N * T;
-    const int cond0 = nb == 1 ? 0 : 1;
-    const int spk_branch = g.spk_dim > 0 ? nb - 1 : -1;
     const int nc = 1 + (g.spk_dim > 0 ? R : 0);
     const long long ML = (6LL * L + 2) * d;
     const int H = g.n_heads, hd = d / H, f = g.ffn_dim;
     const Layout& ly = c->lay;
+    const bool adaptive = op.mode == CFM_GUIDANCE_ADAPTIVE && nb > 1;
 
     float* h = wsp<float>(c, ly.h);
     void* act = c->ws + ly.act;
@@ -470,21 +534,23 @@ cfm_status cfm_sample(cfm_ctx* c, const float* x0, const float* cond, const floa
     float* spkproj = wsp<float>(c, ly.spkproj);
     float* cvec = wsp<float>(c, ly.cvec);
     float* mod = wsp<float>(c, ly.mod);
+    float* xmid = wsp<float>(c, ly.xmid);
     int32_t* kvlen = wsp<int32_t>(c, ly.kvlen);
     uint8_t* kvalid = wsp<uint8_t>(c, ly.kvalid);
     uint8_t* tfull = wsp<uint8_t>(c, ly.tfull);
-    // A masked batch on the bf16 path runs packed: row b*R + r keeps only its
-    // first kv_len[r] frames (up to the last valid one) rounded up to 8 tokens,
-    // rows follow each other, and every token-parallel kernel works on the
-    // packed token count, read on the device. The outputs are those of the
-    // padded layout: every operation but attention is token-local, attention
-    // masks every key from kv_len on, and the frames cut off are masked keys
-    // whose velocities are never used.
-    const bool packed = bf && !prefix && frame_mask != nullptr;
-    const long long NTk = packed ? (long long)N * ((T + 7) / 8 * 8) : NT;   // token capacity
+    // The bf16 channel-condition path runs packed when a batch is masked (row b*R + r
+    // keeps only its first kv_len[r] frames, up to the last valid one, rounded up to
+    // 8 tokens; rows follow each other and every token-parallel kernel works on the
+    // packed token count, read on the device) and under adaptive guidance (the rows
+    // of a request whose unconditional lane has stopped hold no token, so they cost
+    // nothing). The outputs are those of the padded layout: every operation but
+    // attention is token-local, attention masks every key from kv_len on, and the
+    // frames cut off are masked keys whose velocities are never used.
+    const bool packable = bf && !prefix;
+    const bool packed = packable && (frame_mask != nullptr || adaptive);
+    const long long Trow = packed ? (T + 7) / 8 * 8 : T;     // token capacity per row
     int32_t* rowoff = packed ? wsp<int32_t>(c, ly.rowoff) : nullptr;
     int32_t* tokrow = packed ? wsp<int32_t>(c, ly.tokrow) : nullptr;
-    const int32_t* ntok = packed ? rowoff + N : nullptr;
 
     // GEMM through matrix cores (bf16 sampler) or fp32 FMA (fp32 sampler)
     auto gemm = [&](int cls, bool a_f32, const void* A, int lda, Slot w, int M, int Nn, int K, int epi,
@@ -506,19 +572,24 @@ cfm_status cfm_sample(cfm_ctx* c, const float* x0, const float* cond, const floa
         });
     };
 
-    // ---- set-up, once per call
+    // ---- set-up, once per call: key tables, the packed layout of a masked batch,
+    // timestep embeddings and modulation vectors of every evaluation, the condition
+    // projection (constant over steps)
     timed(c, CFM_K_HOISTED, s, [&] {
         launch_key_prep(frame_mask, Tx, nullptr, R, P, T, Tp, kvlen, kvalid, tfull, s);
-        if (packed) launch_pack_rows(kvlen, R, nb, (int)NTk, rowoff, tokrow, s);
+        if (packed && !adaptive) launch_pack_rows(kvlen, nullptr, R, nb, (int)(N * Trow), rowoff, tokrow, s);
+        if (adaptive) launch_fill_i32(lanes, 3 * R, 0, s);
     });
-    timed(c, CFM_K_HOISTED, s, [&] { launch_timestep_embedding(temb, S, g.t_freq_dim, s); });
-    hoisted(false, temb, g.t_freq_dim, c->t1w, c->t1b, S, d, g.t_freq_dim, tpre, d);
-    hoisted(true, tpre, d, c->t2w, c->t2b, S, d, d, ct, d);
+    timed(c, CFM_K_HOISTED, s, [&] {
+        launch_timestep_embedding(temb, n_eval, g.t_freq_dim, op.schedule, S, op.native, per_step, s);
+    });
+    hoisted(false, temb, g.t_freq_dim, c->t1w, c->t1b, n_eval, d, g.t_freq_dim, tpre, d);
+    hoisted(true, tpre, d, c->t2w, c->t2b, n_eval, d, d, ct, d);
     if (g.spk_dim > 0) hoisted(false, spk, g.spk_dim, c->spkw, c->spkb, R, d, g.spk_dim, spkproj, d);
     timed(c, CFM_K_HOISTED, s, [&] {
-        launch_assemble_cvec(ct, g.spk_dim > 0 ? wp<float>(c, c->spkb) : nullptr, spkproj, S, nc, d, cvec, s);
+        launch_assemble_cvec(ct, g.spk_dim > 0 ? wp<float>(c, c->spkb) : nullptr, spkproj, n_eval, nc, d, cvec, s);
     });
-    hoisted(true, cvec, d, c->adaw, c->adab, S * nc, (int)ML, d, mod, ML);
+    hoisted(true, cvec, d, c->adaw, c->adab, n_eval * nc, (int)ML, d, mod, ML);
     {
         EpiParams ep;
         ep.bias = wp<float>(c, c->inb);
@@ -528,42 +599,45 @@ cfm_status cfm_sample(cfm_ctx* c, const float* x0, const float* cond, const floa
         else gemm(CFM_K_HOISTED, true, cond, g.cond_dim, c->incw, R * Tx, d, g.cond_dim, EPI_F32, ep);
     }
 
-    auto rowmod = [&](const float* base, int tokens_per_row) {
-        RowMod m;
-        m.base = base;
-        m.cvec_stride = ML;
-        m.tokens_per_row = tokens_per_row;
-        m.n_requests = R;
-        m.spk_branch = spk_branch;
-        m.tok_row = tokrow;
-        return m;
-    };
-    float w[3] = {1.0f, 0.0f, 0.0f};
-    if (nb == 2) { w[0] = 1.0f - scales[0]; w[1] = scales[0]; }
-    if (nb == 3) { w[0] = 1.0f - scales[0]; w[1] = scales[0] - scales[1]; w[2] = scales[1]; }
-
-    AttnParams ap;
-    ap.qkv = big; ap.vt = vt; ap.Tp = Tp; ap.o = act; ap.rows = N; ap.T = T; ap.H = H; ap.hd = hd;
-    ap.kv_len = kvlen; ap.kv_mod = R; ap.key_mask = frame_mask; ap.mask_stride = Tx; ap.P = P;
-    ap.kvalid = kvalid; ap.tile_full = tfull; ap.row_off = rowoff;
-
-    // ---- Euler steps
-    for (int k = 0; k < S; ++k) {
-        const double t0 = (double)k / S, t1 = (double)(k + 1) / S;
-        const float dt = (float)(t1 - t0);
-        const float* modk = mod + (long long)k * nc * ML;
+    // One estimator evaluation at evaluation index j over nbe branch rows per
+    // request (nbe = nb, or 1: the fully conditioned branch alone, an unguided
+    // evaluation), latent input xl [R, Tx, C]; velocities to vel [nbe, R, Tx, C].
+    // Rows are branch-major (row = b * R + r): with nbe = 1 the single row of a
+    // request is row r, and in the packed layout rows 0 .. R - 1 are a prefix of the
+    // layout, whose token count is row_off[R].
+    auto estimate = [&](int j, int nbe, const float* xl) {
+        const int Ne = nbe * R;
+        const int cond0 = nbe == 1 ? 0 : 1;
+        const int spk_branch = g.spk_dim > 0 ? nbe - 1 : -1;
+        const long long NTk = (long long)Ne * Trow;                 // token capacity of the grid
+        const int32_t* ntok = packed ? rowoff + Ne : nullptr;       // packed: device token count
+        const float* modk = mod + (long long)j * nc * ML;
+        auto rowmod = [&](const float* base, int tokens_per_row) {
+            RowMod m;
+            m.base = base;
+            m.cvec_stride = ML;
+            m.tokens_per_row = tokens_per_row;
+            m.n_requests = R;
+            m.spk_branch = spk_branch;
+            m.tok_row = tokrow;
+            return m;
+        };
+        AttnParams ap;
+        ap.qkv = big; ap.vt = vt; ap.Tp = Tp; ap.o = act; ap.rows = Ne; ap.T = T; ap.H = H; ap.hd = hd;
+        ap.kv_len = kvlen; ap.kv_mod = R; ap.key_mask = frame_mask; ap.mask_stride = Tx; ap.P = P;
+        ap.kvalid = kvalid; ap.tile_full = tfull; ap.row_off = rowoff;
         if (prefix)
             timed(c, CFM_K_GEMM_IN, s, [&] {
-                launch_prefix_init(cproj, wp<float>(c, c->inb), R, nb, cond0, P, T, d, h, s);
+                launch_prefix_init(cproj, wp<float>(c, c->inb), R, nbe, cond0, P, T, d, h, s);
             });
         {
             EpiParams ep;
             ep.bias = wp<float>(c, c->inb);
             ep.out = h; ep.ldo = d;
-            ep.R = R; ep.Tx = Tx; ep.T = T; ep.P = P; ep.nb = nb; ep.cond_branch0 = cond0;
+            ep.R = R; ep.Tx = Tx; ep.T = T; ep.P = P; ep.nb = nbe; ep.cond_branch0 = cond0;
             ep.cproj = prefix ? nullptr : cproj;
             ep.row_off = rowoff;
-            gemm(CFM_K_GEMM_IN, true, out, C, c->inxw, R * Tx, d, C, EPI_INPROJ, ep);
+            gemm(CFM_K_GEMM_IN, true, xl, C, c->inxw, R * Tx, d, C, EPI_INPROJ, ep);
         }
         for (int l = 0; l < L; ++l) {
             const auto& W = c->layers[l];
@@ -598,18 +672,72 @@ cfm_status cfm_sample(cfm_ctx* c, const float* x0, const float* cond, const floa
         {
             const float* mf = modk + (long long)L * 6 * d;
             LnParams ln;
-            ln.h = h; ln.y = act; ln.d = d; ln.n_out = (long long)N * Tx; ln.Tin = T; ln.Tout = Tx; ln.off = P;
+            ln.h = h; ln.y = act; ln.d = d; ln.n_out = (long long)Ne * Tx; ln.Tin = T; ln.Tout = Tx; ln.off = P;
             ln.shift = rowmod(mf, Tx); ln.scale = rowmod(mf + d, Tx); ln.out_bf16 = bf;
             if (packed) { ln.n_out = NTk; ln.Tin = ln.Tout = 1; ln.n_dev = ntok; }   // tokens map one to one
             timed(c, CFM_K_ADALN, s, [&] { launch_adaln(ln, s); });
             EpiParams ep; ep.bias = wp<float>(c, c->outb); ep.out = vel; ep.ldo = C;
             ep.R = R; ep.Tx = Tx; ep.mask = frame_mask;
             ep.tok_row = tokrow; ep.row_off = rowoff; ep.m_dev = ntok;
-            gemm(CFM_K_GEMM_OUT, false, act, d, c->outw, packed ? (int)NTk : N * Tx, C, d, EPI_VOUT, ep);
+            gemm(CFM_K_GEMM_OUT, false, act, d, c->outw, packed ? (int)NTk : Ne * Tx, C, d, EPI_VOUT, ep);
         }
-        timed(c, CFM_K_CFG_EULER, s, [&] {
-            launch_cfg_euler(vel, nb, dt * w[0], dt * w[1], dt * w[2], frame_mask, R, Tx, C, out, s);
-        });
+    };
+
+    // guidance weights of a guided evaluation (weights of the branch velocities
+    // that give the guidance equation)
+    float w[3] = {1.0f, 0.0f, 0.0f};
+    if (nb == 2) { w[0] = 1.0f - scales[0]; w[1] = scales[0]; }
+    if (nb == 3) { w[0] = 1.0f - scales[0]; w[1] = scales[0] - scales[1]; w[2] = scales[1]; }
+    // whether an evaluation at time t runs guided (host-decided policies)
+    auto guided_at = [&](double t) {
+        if (nb == 1) return false;
+        if (op.mode == CFM_GUIDANCE_INTERVAL) return op.start <= t && t <= op.end;
+        return true;   // full CFG; adaptive lanes are decided on the device
+    };
+    // x_out = x_in + dt * (guided combine of the nbe rows just evaluated)
+    auto combine = [&](int nbe, float dt, const float* xin, float* xout, const int32_t* lane_off) {
+        CfgEulerArgs a;
+        a.v = vel; a.nb = nbe; a.mask = frame_mask; a.R = R; a.Tx = Tx; a.C = C;
+        a.x_in = xin; a.x_out = xout; a.lane_off = lane_off; a.w_full = dt;
+        if (nbe == 1) a.w0 = dt;
+        else { a.w0 = dt * w[0]; a.w1 = dt * w[1]; a.w2 = dt * w[2]; }
+        timed(c, CFM_K_CFG_EULER, s, [&] { launch_cfg_euler(a, s); });
+    };
+
+    // ---- steps: the grid is rebuilt before the loop (uniform, quadratic, trailing or
+    // a subsequence of a native grid), then one (Euler) or two (midpoint) evaluations
+    // per step; step sizes and guidance weights are kernel arguments
+    long long guided_evals = 0;
+    for (int k = 0; k < S; ++k) {
+        const double t0 = host_grid_time(op.schedule, S, op.native, k);
+        const double t1 = host_grid_time(op.schedule, S, op.native, k + 1);
+        const float dt = (float)(t1 - t0);
+        const int32_t* st_cur = lanes + (k & 1) * 3 * R;        // lane state this step runs with
+        int32_t* st_next = lanes + ((k + 1) & 1) * 3 * R;
+        const int32_t* lane_off = adaptive ? st_cur + R : nullptr;
+        // this step's packed layout: stopped lanes hold no unconditional rows (only
+        // where the layout is packed; elsewhere every row is computed and the stopped
+        // lanes' rows are not used)
+        if (adaptive && packed)
+            timed(c, CFM_K_HOISTED, s, [&] {
+                launch_pack_rows(kvlen, lane_off, R, nb, (int)(N * Trow), rowoff, tokrow, s);
+            });
+        for (int e = 0; e < per_step; ++e) {
+            const int j = k * per_step + e;
+            const double te = host_eval_time(op.schedule, S, op.native, per_step, j);
+            const int nbe = guided_at(te) ? nb : 1;
+            guided_evals += nbe > 1 ? 1 : 0;
+            estimate(j, nbe, e == 0 ? out : xmid);
+            if (adaptive && e == 0)
+                launch_adaptive_update(vel, nb, frame_mask, R, Tx, C, st_cur, st_next, k, op.warmup, op.patience,
+                                       op.threshold, per_step, s);
+            if (per_step == 2 && e == 0) combine(nbe, 0.5f * dt, out, xmid, lane_off);   // half step
+            else combine(nbe, dt, out, out, lane_off);
+        }
+    }
+    if (op.guided_out != nullptr) {
+        if (adaptive) launch_copy_i32(lanes + (S & 1) * 3 * R + 2 * R, op.guided_out, R, s);
+        else launch_fill_i32(op.guided_out, R, (int)guided_evals, s);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(CFM_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
@@ -632,7 +760,10 @@ cfm_status cfm_cfg_euler(const float* v, const float* w, int nb, float dt, const
     }
     if (!std::isfinite(dt)) return fail(CFM_E_VALUE, "non-finite dt");
     (void)hipGetLastError();
-    launch_cfg_euler(v, nb, ww[0], ww[1], ww[2], mask, R, Tx, C, x, (hipStream_t)stream);
+    CfgEulerArgs a;
+    a.v = v; a.nb = nb; a.w0 = ww[0]; a.w1 = ww[1]; a.w2 = ww[2]; a.mask = mask; a.R = R; a.Tx = Tx; a.C = C;
+    a.x_in = x; a.x_out = x;
+    launch_cfg_euler(a, (hipStream_t)stream);
     hipError_t e = hipGetLastError();
     return e == hipSuccess ? CFM_OK : fail(CFM_E_HIP, "launch failed: %s", hipGetErrorString(e));
 }

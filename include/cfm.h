@@ -160,6 +160,65 @@ cfm_status cfm_sample(cfm_ctx* ctx, const float* x0, const float* cond, const fl
                       const uint8_t* frame_mask, int n_requests, int n_frames, int n_steps,
                       const float* guidance, float* out, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Sampler-level options (cfm_sample_ex). Sources: VoiceHub "Diffusion and flow TTS
+ * optimization", sections "Reduce a 50-step sampler before optimizing its
+ * kernels" (the grid is rebuilt before the loop, keeps both endpoints and strict
+ * monotonicity; native / uniform / quadratic / trailing shapes) and "Guidance
+ * reduction" (limited-interval and adaptive CFG, independent per-request lanes),
+ * and its "Active families" table (Euler or midpoint for the F5-TTS family).
+ * The pages give no formulas; the readings implemented here:
+ *   schedules on S steps, u = k / S: UNIFORM t_k = u, QUADRATIC t_k = u^2 (small
+ *     steps near the noise end), TRAILING t_k = 1 - (1 - u)^2 (small steps near the
+ *     data end), NATIVE t_k = round(k N / S) / N (halves up) on a native grid of
+ *     N = native_steps uniform steps (N >= S);
+ *   MIDPOINT: x_k+1 = x_k + dt v(t_k + dt/2, x_k + (dt/2) v(t_k, x_k)): two estimator
+ *     evaluations per step, so n_steps * 2 must not exceed the config's max_steps
+ *     (which bounds estimator evaluations per call);
+ *   INTERVAL guidance: an evaluation at time t runs the CFG branch rows only when
+ *     interval_start <= t <= interval_end; otherwise only the fully conditioned
+ *     branch row of every request is evaluated (half the rows with two branches)
+ *     and its velocity is used as is (guidance scale 1);
+ *   ADAPTIVE guidance, per request: after a step's first evaluation the metric
+ *     sum |v_full - v_u| / sum |v_full| over the request's valid frames is compared
+ *     with adaptive_threshold; steps below adaptive_warmup never count, later steps
+ *     below the threshold increment a counter and others reset it; once the counter
+ *     reaches adaptive_patience the request's unconditional lane stops for all later
+ *     steps, which run the fully conditioned row alone. Decided on the device, with
+ *     no host synchronisation; on the bf16 channel-condition path the stopped rows
+ *     are dropped from the packed row layout, elsewhere they are still computed and
+ *     not used. */
+typedef enum cfm_schedule {
+    CFM_SCHEDULE_UNIFORM = 0, CFM_SCHEDULE_QUADRATIC = 1, CFM_SCHEDULE_TRAILING = 2, CFM_SCHEDULE_NATIVE = 3
+} cfm_schedule;
+typedef enum cfm_solver { CFM_SOLVER_EULER = 0, CFM_SOLVER_MIDPOINT = 1 } cfm_solver;
+typedef enum cfm_guidance_mode {
+    CFM_GUIDANCE_FULL = 0, CFM_GUIDANCE_INTERVAL = 1, CFM_GUIDANCE_ADAPTIVE = 2
+} cfm_guidance_mode;
+
+typedef struct cfm_sample_options {
+    int32_t schedule;            /* cfm_schedule                                         */
+    int32_t native_steps;        /* NATIVE: steps of the native uniform grid (>= n_steps) */
+    int32_t solver;              /* cfm_solver                                           */
+    int32_t guidance_mode;       /* cfm_guidance_mode                                    */
+    float interval_start, interval_end;                 /* INTERVAL (finite)            */
+    float adaptive_threshold;    /* ADAPTIVE: >= 0, +infinity allowed                    */
+    int32_t adaptive_warmup;     /* ADAPTIVE: >= 0                                       */
+    int32_t adaptive_patience;   /* ADAPTIVE: >= 1                                       */
+    int32_t reserved;
+    int32_t* guided_evals;       /* optional device int32 [R]: per request, the number of
+                                    estimator evaluations that ran its unconditional rows */
+} cfm_sample_options;
+
+/* cfm_sample with sampler-level options (NULL = uniform grid, Euler, full CFG,
+ * i.e. exactly cfm_sample). Same arguments, rules and errors as cfm_sample, plus
+ * CFM_E_VALUE for an option out of range and CFM_E_CAPACITY when the estimator
+ * evaluations (n_steps, twice that for MIDPOINT) exceed max_steps. */
+cfm_status cfm_sample_ex(cfm_ctx* ctx, const float* x0, const float* cond, const float* spk,
+                         const uint8_t* frame_mask, int n_requests, int n_frames, int n_steps,
+                         const float* guidance, const cfm_sample_options* options, float* out,
+                         void* stream);
+
 /* Frees host state only: the borrowed weight and workspace buffers stay the
  * caller's (vox-serve, "Adding a Model": buffers are owned by the caller and
  * outlive the captured work). Work already enqueued keeps using them, so the
