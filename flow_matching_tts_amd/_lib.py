@@ -50,7 +50,15 @@ class cfm_sample_options(C.Structure):
     _fields_ = [("schedule", C.c_int32), ("native_steps", C.c_int32), ("solver", C.c_int32),
                 ("guidance_mode", C.c_int32), ("interval_start", C.c_float), ("interval_end", C.c_float),
                 ("adaptive_threshold", C.c_float), ("adaptive_warmup", C.c_int32),
-                ("adaptive_patience", C.c_int32), ("reserved", C.c_int32), ("guided_evals", C.c_void_p)]
+                ("adaptive_patience", C.c_int32), ("reserved", C.c_int32), ("guided_evals", C.c_void_p),
+                ("cache", C.c_int32), ("cache_front", C.c_int32), ("cache_back", C.c_int32),
+                ("cache_warmup", C.c_int32), ("cache_max_consecutive", C.c_int32),
+                ("cache_max_cached", C.c_int32), ("cache_threshold", C.c_float), ("cache_budget", C.c_float),
+                ("cache_force", C.c_void_p), ("cache_hits", C.c_void_p)]
+
+
+CACHE_DEFAULTS = dict(front=1, back=1, warmup=3, max_consecutive=2, max_cached=-1, threshold=0.05, budget=0.12,
+                      force=())
 
 
 class CfmError(RuntimeError):
@@ -288,13 +296,15 @@ class Sampler:
     def sample(self, x0, cond, *, mask=None, spk=None, n_steps: int, guidance: Sequence[float] = (),
                out=None, stream=None, schedule: str = "uniform", native_steps: Optional[int] = None,
                solver: str = "euler", guidance_mode: str = "full", interval=(0.0, 1.0),
-               adaptive=(0.015, 4, 2), guided_evals=None):
+               adaptive=(0.015, 4, 2), guided_evals=None, cache=None, cache_hits=None):
         """out[R, Tx, C] (fp32, device) after n_steps solver steps; out may be x0 itself.
 
         schedule / native_steps / solver / guidance_mode / interval / adaptive
         (threshold, warmup, patience) select the sampler-level options of
         cfm_sample_ex; guided_evals, an int32 [R] device tensor, receives per request
-        the number of evaluations that ran its unconditional rows."""
+        the number of evaluations that ran its unconditional rows. cache (a dict over
+        CACHE_DEFAULTS' keys; None = off) turns on the block-residual cache, and
+        cache_hits, an int32 [1] device tensor, receives its number of hits."""
         import torch
         guidance = tuple(guidance)
         evals = int(n_steps) * (2 if solver == "midpoint" else 1)
@@ -309,12 +319,28 @@ class Sampler:
                                  ("guidance_mode", guidance_mode, GUIDANCE_MODES)):
             if val not in table:
                 raise ValueError(f"{name} {val!r} not one of {sorted(table)}")
+        if cache_hits is not None:
+            _need("cache_hits", cache_hits, (1,), torch.int32)
+            _on_device(x0=x0, cache_hits=cache_hits)
         if out is None:
             out = torch.empty_like(x0)
         g = (C.c_float * max(1, len(guidance)))(*[float(v) for v in guidance])
         opt = cfm_sample_options(SCHEDULES[schedule], int(native_steps or 0), SOLVERS[solver],
                                  GUIDANCE_MODES[guidance_mode], float(interval[0]), float(interval[1]),
                                  float(adaptive[0]), int(adaptive[1]), int(adaptive[2]), 0, _ptr(guided_evals))
+        force = None
+        if cache is not None:
+            unknown = set(cache) - set(CACHE_DEFAULTS)
+            if unknown:
+                raise ValueError(f"unknown cache options {sorted(unknown)}")
+            cc = dict(CACHE_DEFAULTS, **cache)
+            force = (C.c_uint8 * max(1, evals))(*[1 if v else 0 for v in list(cc["force"])[:evals]])
+            opt.cache, opt.cache_front, opt.cache_back = 1, int(cc["front"]), int(cc["back"])
+            opt.cache_warmup, opt.cache_max_consecutive = int(cc["warmup"]), int(cc["max_consecutive"])
+            opt.cache_max_cached = int(cc["max_cached"])
+            opt.cache_threshold, opt.cache_budget = float(cc["threshold"]), float(cc["budget"])
+            opt.cache_force = C.cast(force, C.c_void_p)
+        opt.cache_hits = _ptr(cache_hits)
         check(load().cfm_sample_ex(self._ctx, _ptr(x0), _ptr(cond), _ptr(spk), _ptr(mask), R, Tx,
                                    int(n_steps), g, C.byref(opt), _ptr(out), _stream(stream)))
         return out

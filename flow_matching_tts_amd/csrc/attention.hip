@@ -106,6 +106,7 @@ attn_bf16_kernel(AttnParams p) {
     uint8_t* const kvs = (uint8_t*)(kbias + NS * KT);               // Tp validity bytes, then tile flags
     const unsigned ring_addr = (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)asmem;
 
+    if (p.active != nullptr && *p.active == 0) return;   // skipped (block-uniform)
     const int row = blockIdx.z, head = blockIdx.y;
     // the wave index picks the load instructions: keep it in a scalar register
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -363,6 +364,7 @@ attn_short_kernel(AttnParams p) {
     __shared__ __attribute__((aligned(16))) bf16 Vt[2][HD * VP];
     __shared__ float kbias[2][KT];
 
+    if (p.active != nullptr && *p.active == 0) return;   // skipped (block-uniform)
     const int row = blockIdx.z, head = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int j = lane & 31, h = lane >> 5;
@@ -518,6 +520,7 @@ attn_f32_kernel(AttnParams p) {
     __shared__ float Kt[FKT][HD_ + 1];
     __shared__ float Vs[FKT][HD_ + 1];
     __shared__ float kb[FKT];
+    if (p.active != nullptr && *p.active == 0) return;   // skipped (block-uniform)
     const int row = blockIdx.z, head = blockIdx.y;
     const int q = blockIdx.x * FQ + threadIdx.x;
     const int T = p.T, d = p.H * HD_;

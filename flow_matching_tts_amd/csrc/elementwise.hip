@@ -96,6 +96,97 @@ adaptive_update_kernel(const float* __restrict__ v, int nb, long long branch_str
     }
 }
 
+// ---------------------------------------------------------------------------
+// Block-residual cache (one lane: the whole batch of a call). The probe is the
+// hidden state after the front blocks; its score against the previous
+// evaluation's probe is sum |h - prev| / sum |prev| over valid tokens, reduced in a
+// fixed order (per-thread strided sums, an LDS tree per block, the blocks' partials
+// summed by one block), so that every run takes the same decisions.
+__device__ __forceinline__ bool cache_token_valid(const CacheTok& tk, long long m) {
+    int row, t;
+    if (tk.tok_row != nullptr) {
+        row = tk.tok_row[m];
+        if (row < 0) return false;
+        t = (int)(m - tk.row_off[row]);
+    } else {
+        row = (int)(m / tk.T);
+        t = (int)(m - (long long)row * tk.T);
+    }
+    return t < tk.Tp && tk.kvalid[(long long)(row % tk.R) * tk.Tp + t] != 0;
+}
+
+constexpr int CS_NT = 256;
+__global__ void __launch_bounds__(CS_NT)
+cache_score_kernel(const f32x4* __restrict__ h, f32x4* __restrict__ prev, int d4, CacheTok tk, float* parts) {
+    __shared__ float sn[CS_NT], sd[CS_NT];
+    const long long ntok = tk.n_dev ? min(tk.cap, (long long)*tk.n_dev) : tk.cap;
+    const long long n = ntok * d4;
+    float num = 0.0f, den = 0.0f;
+    for (long long e = (long long)blockIdx.x * CS_NT + threadIdx.x; e < n; e += (long long)gridDim.x * CS_NT) {
+        const f32x4 a = h[e], b = prev[e];
+        if (cache_token_valid(tk, e / d4)) {
+            const f32x4 df = a - b;
+            num += (fabsf(df[0]) + fabsf(df[1])) + (fabsf(df[2]) + fabsf(df[3]));
+            den += (fabsf(b[0]) + fabsf(b[1])) + (fabsf(b[2]) + fabsf(b[3]));
+        }
+        prev[e] = a;
+    }
+    sn[threadIdx.x] = num;
+    sd[threadIdx.x] = den;
+    __syncthreads();
+    for (int o = CS_NT / 2; o > 0; o >>= 1) {
+        if ((int)threadIdx.x < o) { sn[threadIdx.x] += sn[threadIdx.x + o]; sd[threadIdx.x] += sd[threadIdx.x + o]; }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) { parts[2 * blockIdx.x] = sn[0]; parts[2 * blockIdx.x + 1] = sd[0]; }
+}
+
+__global__ void __launch_bounds__(CS_NT)
+cache_decide_kernel(const float* parts, int32_t* st, int forced, float threshold, float budget, int max_consecutive,
+                    int max_cached, CacheTok tk) {
+    __shared__ float sn[CS_NT], sd[CS_NT];
+    float num = 0.0f, den = 0.0f;
+    for (int i = threadIdx.x; i < kCacheParts; i += CS_NT) { num += parts[2 * i]; den += parts[2 * i + 1]; }
+    sn[threadIdx.x] = num;
+    sd[threadIdx.x] = den;
+    __syncthreads();
+    for (int o = CS_NT / 2; o > 0; o >>= 1) {
+        if ((int)threadIdx.x < o) { sn[threadIdx.x] += sn[threadIdx.x + o]; sd[threadIdx.x] += sd[threadIdx.x + o]; }
+        __syncthreads();
+    }
+    if (threadIdx.x != 0) return;
+    const int consecutive = st[1], hits = st[2], has_res = st[3], has_prev = st[6];
+    const float acc = __int_as_float(st[7]);
+    const float score = has_prev ? (sd[0] > 0.0f ? sn[0] / sd[0] : 0.0f) : __builtin_nanf("");
+    const bool compute = forced || !has_res || (max_cached >= 0 && hits >= max_cached) ||
+                         consecutive >= max_consecutive || !(score < threshold) || acc + score > budget;
+    st[0] += 1;
+    if (compute) {
+        st[1] = 0;
+        st[3] = 1;                          // the residual is saved after the middle blocks
+        st[7] = __float_as_int(0.0f);
+    } else {
+        st[1] = consecutive + 1;
+        st[2] = hits + 1;
+        st[7] = __float_as_int(acc + score);
+    }
+    st[4] = compute ? 1 : 0;
+    st[5] = compute ? (int)(tk.n_dev ? min(tk.cap, (long long)*tk.n_dev) : tk.cap) : 0;
+    st[6] = 1;
+}
+
+__global__ void __launch_bounds__(256)
+cache_apply_kernel(f32x4* __restrict__ h, f32x4* __restrict__ res, const f32x4* __restrict__ prev, int d4, CacheTok tk,
+                   const int32_t* st) {
+    const long long ntok = tk.n_dev ? min(tk.cap, (long long)*tk.n_dev) : tk.cap;
+    const long long n = ntok * d4;
+    const bool compute = st[4] != 0;
+    for (long long e = (long long)blockIdx.x * 256 + threadIdx.x; e < n; e += (long long)gridDim.x * 256) {
+        if (compute) res[e] = h[e] - prev[e];
+        else h[e] = h[e] + res[e];
+    }
+}
+
 __global__ void fill_i32_kernel(int32_t* p, int n, int value) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) p[i] = value;
@@ -363,6 +454,22 @@ void launch_adaptive_update(const float* v, int nb, const uint8_t* mask, int R, 
     if (R <= 0) return;
     adaptive_update_kernel<<<R, AG_NT, 0, s>>>(v, nb, (long long)R * Tx * C, mask, Tx, C, st_in, st_out, R, step,
                                                warmup, patience, threshold, evals_per_step);
+}
+
+void launch_cache_score(const float* h, float* prev, int d, const CacheTok& tk, float* parts, hipStream_t s) {
+    cache_score_kernel<<<kCacheParts, CS_NT, 0, s>>>((const f32x4*)h, (f32x4*)prev, d / 4, tk, parts);
+}
+
+void launch_cache_decide(const float* parts, int32_t* state, int forced, float threshold, float budget,
+                         int max_consecutive, int max_cached, const CacheTok& tk, hipStream_t s) {
+    cache_decide_kernel<<<1, CS_NT, 0, s>>>(parts, state, forced, threshold, budget, max_consecutive, max_cached, tk);
+}
+
+void launch_cache_apply(float* h, float* res, const float* prev, int d, const CacheTok& tk, const int32_t* state,
+                        hipStream_t s) {
+    const long long n = tk.cap * (d / 4);
+    const int blocks = (int)std::min<long long>(4096, (n + 255) / 256);
+    if (blocks > 0) cache_apply_kernel<<<blocks, 256, 0, s>>>((f32x4*)h, (f32x4*)res, (const f32x4*)prev, d / 4, tk, state);
 }
 
 void launch_fill_i32(int32_t* p, int n, int value, hipStream_t s) {

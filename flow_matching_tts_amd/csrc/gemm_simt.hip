@@ -25,6 +25,10 @@ gemm_simt_kernel(const float* __restrict__ A, int lda, const WT* __restrict__ W,
     const int tid = threadIdx.x;
     const int tx = tid & 15, ty = tid >> 4;
     const int m0 = blockIdx.y * TM, n0 = blockIdx.x * TN;
+    if (ep.m_dev) {                 // device row count (at most M): whole block, before any barrier
+        M = min(M, *ep.m_dev);
+        if (m0 >= M) return;
+    }
     float acc[4][4] = {};
 
     for (int k0 = 0; k0 < K; k0 += TK) {

@@ -72,6 +72,8 @@ struct AttnParams {
     // packed rows: row i's q|k rows start at token row_off[i] (else i * T); the
     // row's query count is then its key length
     const int32_t* row_off = nullptr;
+    // optional device flag: when it reads 0 every block exits at once (a skipped block)
+    const int32_t* active = nullptr;
 };
 void launch_attention_bf16(const AttnParams& p, hipStream_t s);
 // whether the bf16 attention's LDS (key ring plus per-key tables) holds sequences of T keys
@@ -111,6 +113,27 @@ void launch_adaptive_update(const float* v, int nb, const uint8_t* mask, int R, 
                             int32_t* st_out, int step, int warmup, int patience, float threshold, int evals_per_step,
                             hipStream_t s);
 void launch_fill_i32(int32_t* p, int n, int value, hipStream_t s);
+// Block-residual cache (one lane per call). State: int32 [8] = evaluations, consecutive
+// hits, hits, residual saved, compute flag, middle-block token count, probe saved,
+// accumulated score (float bits). kCacheParts partial sums per score.
+constexpr int kCacheParts = 512;
+struct CacheTok {              // which tokens of the hidden state exist and are valid frames
+    long long cap = 0;         // token capacity (grid size)
+    const int32_t* n_dev = nullptr;   // device token count (packed layout) or null: cap tokens
+    int T = 1;                 // tokens per row (padded layout)
+    const int32_t* tok_row = nullptr, *row_off = nullptr;   // packed layout
+    const uint8_t* kvalid = nullptr;  // [R, Tp] key validity
+    int R = 1, Tp = 64;
+};
+// partial sums of |h - prev| and |prev| over valid tokens (parts [kCacheParts][2]); then prev = h
+void launch_cache_score(const float* h, float* prev, int d, const CacheTok& tk, float* parts, hipStream_t s);
+// the decision of one evaluation from the partial sums (reads the token count for the
+// middle blocks from tk.n_dev, or uses tk.cap)
+void launch_cache_decide(const float* parts, int32_t* state, int forced, float threshold, float budget,
+                         int max_consecutive, int max_cached, const CacheTok& tk, hipStream_t s);
+// after the middle blocks: compute flag set -> res = h - prev; else h += res
+void launch_cache_apply(float* h, float* res, const float* prev, int d, const CacheTok& tk, const int32_t* state,
+                        hipStream_t s);
 void launch_copy_i32(const int32_t* src, int32_t* dst, int n, hipStream_t s);
 // Evaluation times of a sampling call: grid kind 0 uniform, 1 quadratic, 2 trailing,
 // 3 native subsequence of N uniform steps; per_step evaluations per step (1 Euler,

@@ -187,7 +187,7 @@ Slot find(const Manifest& m, const char* name, long long col0 = 0) {
 
 struct Layout {   // workspace regions, byte offsets
     size_t h, act, big, vt, v, cproj, temb, tpre, ct, spkproj, cvec, mod, kvlen, kvalid, tfull, rowoff, tokrow,
-        xmid, lanes, total;
+        xmid, lanes, probe, resid, cstate, cparts, total;
 };
 
 inline long long round64(long long v) { return (v + 63) / 64 * 64; }
@@ -228,6 +228,10 @@ Layout plan_workspace(const cfm_config& c) {
     L.tokrow = take(packable ? N * TT * 4 : 0);
     L.xmid = take(Rm * Tx * c.latent_dim * 4);          // midpoint solver: x at the half step
     L.lanes = take(2 * 3 * Rm * 4);                      // adaptive guidance: two states [count | off | guided]
+    L.probe = take(N * TT * d * 4);                      // block-residual cache: previous probe
+    L.resid = take(N * TT * d * 4);                      // ... and the saved middle-block residual
+    L.cstate = take(8 * 4);
+    L.cparts = take(kCacheParts * 2 * 4);
     L.total = off;
     return L;
 }
@@ -420,6 +424,11 @@ struct Opts {                  // validated cfm_sample_options
     float threshold = 0.0f;
     int warmup = 0, patience = 1;
     int32_t* guided_out = nullptr;
+    bool cache = false;
+    int c_front = 1, c_back = 1, c_warmup = 0, c_consec = 0, c_max = -1;
+    float c_threshold = 0.0f, c_budget = 0.0f;
+    const uint8_t* c_force = nullptr;
+    int32_t* c_hits = nullptr;
 };
 
 cfm_status read_options(const cfm_sample_options* o, int S, Opts& out) {
@@ -450,6 +459,27 @@ cfm_status read_options(const cfm_sample_options* o, int S, Opts& out) {
     out.warmup = o->adaptive_warmup;
     out.patience = o->adaptive_patience;
     out.guided_out = o->guided_evals;
+    out.c_hits = o->cache_hits;
+    if (o->cache != 0) {
+        if (o->cache != 1) return fail(CFM_E_VALUE, "cache %d", o->cache);
+        if (o->guidance_mode != CFM_GUIDANCE_FULL)
+            return fail(CFM_E_UNSUPPORTED, "the block-residual cache needs guidance_mode FULL");
+        if (o->cache_front < 1 || o->cache_back < 0 || o->cache_warmup < 0 || o->cache_max_consecutive < 0 ||
+            o->cache_max_cached < -1)
+            return fail(CFM_E_VALUE, "cache block counts / warm-up / limits out of range");
+        if (std::isnan(o->cache_threshold) || o->cache_threshold < 0.0f || std::isnan(o->cache_budget) ||
+            o->cache_budget < 0.0f)
+            return fail(CFM_E_VALUE, "cache threshold and budget must be >= 0 (infinity allowed)");
+        out.cache = true;
+        out.c_front = o->cache_front;
+        out.c_back = o->cache_back;
+        out.c_warmup = o->cache_warmup;
+        out.c_consec = o->cache_max_consecutive;
+        out.c_max = o->cache_max_cached;
+        out.c_threshold = o->cache_threshold;
+        out.c_budget = o->cache_budget;
+        out.c_force = o->cache_force;
+    }
     return CFM_OK;
 }
 
@@ -490,8 +520,8 @@ cfm_status cfm_sample_ex(cfm_ctx* c, const float* x0, const float* cond, const f
     if (g.spk_dim > 0 && spk == nullptr) return fail(CFM_E_NULL, "spk is NULL");
     if (!aligned16(x0) || !aligned16(out) || !aligned16(cond) || (spk && !aligned16(spk)))
         return fail(CFM_E_SHAPE, "x0, cond, spk and out must be 16-byte aligned");
-    if (op.guided_out != nullptr && ((uintptr_t)op.guided_out & 3))
-        return fail(CFM_E_SHAPE, "guided_evals must be 4-byte aligned");
+    if ((op.guided_out != nullptr && ((uintptr_t)op.guided_out & 3)) || (op.c_hits && ((uintptr_t)op.c_hits & 3)))
+        return fail(CFM_E_SHAPE, "guided_evals and cache_hits must be 4-byte aligned");
     const int C = g.latent_dim, d = g.d_model, L = g.n_layers;
     const size_t xbytes = (size_t)R * Tx * C * sizeof(float);
     {
@@ -507,6 +537,7 @@ cfm_status cfm_sample_ex(cfm_ctx* c, const float* x0, const float* cond, const f
     int32_t* lanes = wsp<int32_t>(c, c->lay.lanes);   // two adaptive states of 3R ints
     if (S == 0) {
         if (op.guided_out) launch_fill_i32(op.guided_out, R, 0, s);
+        if (op.c_hits) launch_fill_i32(op.c_hits, 1, 0, s);
         hipError_t e = hipGetLastError();
         return e == hipSuccess ? CFM_OK : fail(CFM_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     }
@@ -535,6 +566,13 @@ cfm_status cfm_sample_ex(cfm_ctx* c, const float* x0, const float* cond, const f
     float* cvec = wsp<float>(c, ly.cvec);
     float* mod = wsp<float>(c, ly.mod);
     float* xmid = wsp<float>(c, ly.xmid);
+    float* probe = wsp<float>(c, ly.probe);
+    float* resid = wsp<float>(c, ly.resid);
+    int32_t* cstate = wsp<int32_t>(c, ly.cstate);
+    float* cparts = wsp<float>(c, ly.cparts);
+    // block-residual cache: front blocks [0, cf), middle [cf, cb), back [cb, L)
+    const int cf = std::min(op.c_front, L), cb = std::max(cf, L - op.c_back);
+    const bool caching = op.cache && cf < cb;
     int32_t* kvlen = wsp<int32_t>(c, ly.kvlen);
     uint8_t* kvalid = wsp<uint8_t>(c, ly.kvalid);
     uint8_t* tfull = wsp<uint8_t>(c, ly.tfull);
@@ -579,6 +617,7 @@ cfm_status cfm_sample_ex(cfm_ctx* c, const float* x0, const float* cond, const f
         launch_key_prep(frame_mask, Tx, nullptr, R, P, T, Tp, kvlen, kvalid, tfull, s);
         if (packed && !adaptive) launch_pack_rows(kvlen, nullptr, R, nb, (int)(N * Trow), rowoff, tokrow, s);
         if (adaptive) launch_fill_i32(lanes, 3 * R, 0, s);
+        if (op.cache) launch_fill_i32(cstate, 8, 0, s);
     });
     timed(c, CFM_K_HOISTED, s, [&] {
         launch_timestep_embedding(temb, n_eval, g.t_freq_dim, op.schedule, S, op.native, per_step, s);
@@ -639,35 +678,55 @@ cfm_status cfm_sample_ex(cfm_ctx* c, const float* x0, const float* cond, const f
             ep.row_off = rowoff;
             gemm(CFM_K_GEMM_IN, true, xl, C, c->inxw, R * Tx, d, C, EPI_INPROJ, ep);
         }
+        CacheTok tk;
+        tk.cap = NTk; tk.n_dev = ntok; tk.T = T; tk.tok_row = tokrow; tk.row_off = rowoff; tk.kvalid = kvalid;
+        tk.R = R; tk.Tp = Tp;
         for (int l = 0; l < L; ++l) {
+            if (caching && l == cf) {
+                // probe: the state after the front blocks, scored against the previous one
+                timed(c, CFM_K_HOISTED, s, [&] {
+                    launch_cache_score(h, probe, d, tk, cparts, s);
+                    const int forced = j < op.c_warmup || (op.c_force != nullptr && op.c_force[j] != 0);
+                    launch_cache_decide(cparts, cstate, forced, op.c_threshold, op.c_budget, op.c_consec, op.c_max,
+                                        tk, s);
+                });
+            }
+            // middle blocks under the cache: their kernels read the token count the
+            // decision left (0 on a hit: every block exits at once)
+            const bool mid = caching && l >= cf && l < cb;
+            const int32_t* ntok_l = mid ? cstate + 5 : ntok;
             const auto& W = c->layers[l];
             const float* ml = modk + (long long)l * 6 * d;
             LnParams ln;
             ln.h = h; ln.y = act; ln.d = d; ln.n_out = NTk; ln.Tin = T; ln.Tout = T; ln.off = 0;
             ln.shift = rowmod(ml + 0 * d, T); ln.scale = rowmod(ml + 1 * d, T); ln.out_bf16 = bf;
-            ln.n_dev = ntok;
+            ln.n_dev = ntok_l;
             timed(c, CFM_K_ADALN, s, [&] { launch_adaln(ln, s); });
             EpiParams e1; e1.bias = wp<float>(c, W.qkvb); e1.out = big;
             if (bf) {   // q|k rows of 2d, v transposed per head for the attention tiles
                 e1.ldo = 2 * d; e1.vt = vt; e1.H = H; e1.T = T; e1.Tp = Tp; e1.d2 = 2 * d;
-                e1.tok_row = tokrow; e1.row_off = rowoff; e1.m_dev = ntok;
+                e1.tok_row = tokrow; e1.row_off = rowoff; e1.m_dev = ntok_l;
             } else {
                 e1.ldo = 3 * d;
+                e1.m_dev = ntok_l;
             }
             gemm(CFM_K_GEMM_QKV, false, act, d, W.qkvw, (int)NTk, 3 * d, d, bf ? EPI_QKV : EPI_ACT, e1);
+            ap.active = mid ? cstate + 4 : nullptr;
             timed(c, CFM_K_ATTENTION, s, [&] {
                 if (bf) launch_attention_bf16(ap, s); else launch_attention_f32(ap, s);
             });
             EpiParams e2; e2.bias = wp<float>(c, W.projb); e2.out = h; e2.ldo = d; e2.gate = rowmod(ml + 2 * d, T);
-            e2.m_dev = ntok;
+            e2.m_dev = ntok_l;
             gemm(CFM_K_GEMM_PROJ, false, act, d, W.projw, (int)NTk, d, d, EPI_GATED, e2);
             ln.shift = rowmod(ml + 3 * d, T); ln.scale = rowmod(ml + 4 * d, T);
             timed(c, CFM_K_ADALN, s, [&] { launch_adaln(ln, s); });
-            EpiParams e3; e3.bias = wp<float>(c, W.fc1b); e3.out = big; e3.ldo = f; e3.m_dev = ntok;
+            EpiParams e3; e3.bias = wp<float>(c, W.fc1b); e3.out = big; e3.ldo = f; e3.m_dev = ntok_l;
             gemm(CFM_K_GEMM_FC1, false, act, d, W.fc1w, (int)NTk, f, d, EPI_GELU_ACT, e3);
             EpiParams e4; e4.bias = wp<float>(c, W.fc2b); e4.out = h; e4.ldo = d; e4.gate = rowmod(ml + 5 * d, T);
-            e4.m_dev = ntok;
+            e4.m_dev = ntok_l;
             gemm(CFM_K_GEMM_FC2, false, big, f, W.fc2w, (int)NTk, d, f, EPI_GATED, e4);
+            if (caching && l == cb - 1)   // computed: save the residual; hit: add the saved one
+                timed(c, CFM_K_HOISTED, s, [&] { launch_cache_apply(h, resid, probe, d, tk, cstate, s); });
         }
         {
             const float* mf = modk + (long long)L * 6 * d;
@@ -738,6 +797,10 @@ cfm_status cfm_sample_ex(cfm_ctx* c, const float* x0, const float* cond, const f
     if (op.guided_out != nullptr) {
         if (adaptive) launch_copy_i32(lanes + (S & 1) * 3 * R + 2 * R, op.guided_out, R, s);
         else launch_fill_i32(op.guided_out, R, (int)guided_evals, s);
+    }
+    if (op.c_hits != nullptr) {
+        if (caching) launch_copy_i32(cstate + 2, op.c_hits, 1, s);
+        else launch_fill_i32(op.c_hits, 1, 0, s);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(CFM_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));

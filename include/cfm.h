@@ -187,7 +187,21 @@ cfm_status cfm_sample(cfm_ctx* ctx, const float* x0, const float* cond, const fl
  *     steps, which run the fully conditioned row alone. Decided on the device, with
  *     no host synchronisation; on the bf16 channel-condition path the stopped rows
  *     are dropped from the packed row layout, elsewhere they are still computed and
- *     not used. */
+ *     not used.
+ * Block-residual caching (VoiceHub, section "Approximate block-residual caching"),
+ * readings: the cache lane is the whole batch of one call (the packed CFG batch);
+ * every estimator evaluation is a cache step; the probe is the hidden state after
+ * the first cache_front blocks, scored against the previous evaluation's probe as
+ * sum |probe - prev| / sum |prev| over valid frames; an evaluation computes the
+ * middle blocks when forced (cache_force, or one of the first cache_warmup
+ * evaluations), when no residual is saved yet, when cache_max_cached hits have been
+ * taken, after cache_max_consecutive hits in a row, when the score is not below
+ * cache_threshold, or when the scores accepted since the last computation plus this
+ * one exceed cache_budget; a computing evaluation saves the middle blocks' residual
+ * (state after minus state before), a hit adds it instead of running them. The
+ * last cache_back blocks always run. Decided on the device (no host
+ * synchronisation); skipped blocks' kernels exit at once. Needs guidance_mode FULL
+ * (a changing row set would invalidate the probe), else CFM_E_UNSUPPORTED. */
 typedef enum cfm_schedule {
     CFM_SCHEDULE_UNIFORM = 0, CFM_SCHEDULE_QUADRATIC = 1, CFM_SCHEDULE_TRAILING = 2, CFM_SCHEDULE_NATIVE = 3
 } cfm_schedule;
@@ -208,6 +222,18 @@ typedef struct cfm_sample_options {
     int32_t reserved;
     int32_t* guided_evals;       /* optional device int32 [R]: per request, the number of
                                     estimator evaluations that ran its unconditional rows */
+    /* Block-residual cache (DBCache; 0 = off): see the reading below.               */
+    int32_t cache;               /* 1 = on                                               */
+    int32_t cache_front;         /* Fn >= 1 blocks always run first                      */
+    int32_t cache_back;          /* Bn >= 0 blocks always run last                       */
+    int32_t cache_warmup;        /* the first evaluations that always compute (>= 0)     */
+    int32_t cache_max_consecutive;  /* hits in a row before a forced computation (>= 0)  */
+    int32_t cache_max_cached;    /* total hits allowed per call, -1 = unlimited          */
+    float cache_threshold;       /* hit when the probe score is below it (>= 0, inf ok)  */
+    float cache_budget;          /* refresh when accepted scores add up past it (>= 0)   */
+    const uint8_t* cache_force;  /* optional host [evaluations]: nonzero forces computing */
+    int32_t* cache_hits;         /* optional device int32 [1]: evaluations that reused the
+                                    saved residual                                       */
 } cfm_sample_options;
 
 /* cfm_sample with sampler-level options (NULL = uniform grid, Euler, full CFG,
