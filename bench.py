@@ -95,7 +95,31 @@ def cfg_euler_cold(s, reps: int = 20):
             "reps": reps}
 
 
+def host_description():
+    """CPU model and the numpy BLAS build the oracle runs on."""
+    model = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = "unknown"
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [f"{i.get('internal_api')} {i.get('version')}" for i in threadpool_info() if i.get("user_api") == "blas"]
+        blas = ", ".join(libs) or blas
+    except Exception:
+        pass
+    return model, f"numpy {np.__version__}, BLAS {blas}"
+
+
 def cpu_baseline(s, W, I, max_workers: int):
+    """The fp64 oracle on a bounded sample of the workload: one Euler step (of the
+    workload's S) for as many requests as there are worker processes (one request per
+    process, one BLAS thread each), scaled to estimator evals/s like the GPU figure."""
     from oracle import sampler as O
     cores = max(1, min(O.host_cores(), max_workers, s.n_requests))
     reqs = list(range(cores))
@@ -103,11 +127,12 @@ def cpu_baseline(s, W, I, max_workers: int):
     O.sample(W, s, I["x0"], I["cond"], I["spk"], I["mask"], 1, s.guidance, requests=reqs, workers=cores)
     t = time.perf_counter() - t0
     evals = len(reqs) * s.n_branches * 1
+    model, blas = host_description()
     return {"value": evals / t, "unit": "estimator evals/s", "cores": cores, "kind": "oracle",
-            "sample": f"{s.name}: {len(reqs)} requests x 1 Euler step = {evals} row-evaluations of "
-                      f"{s.seq_len} frames, fp64 numpy oracle, one process per request with 1 BLAS "
-                      f"thread; {t:.1f} s wall on {platform.processor() or platform.machine()}",
-            "seconds": t}
+            "sample": f"{s.name}: 1 of {s.n_steps} Euler steps for {len(reqs)} of {s.n_requests} requests = "
+                      f"{evals} row-evaluations of {s.seq_len} frames; fp64 numpy oracle, one process per "
+                      f"request with 1 BLAS thread; {t:.1f} s wall",
+            "cpu": model, "numpy_blas": blas, "host_cores": O.host_cores(), "seconds": t}
 
 
 PROBE_BYTES = 1 << 30     # bytes read (and written) by one launch of the copy probe
@@ -167,6 +192,16 @@ def main():
     ap.add_argument("--no-kernel-timing", action="store_true")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="only copy a known number of bytes (calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one sampling call in a HIP graph and time its replays")
+    ap.add_argument("--schedule", default="uniform", choices=["uniform", "quadratic", "trailing", "native"])
+    ap.add_argument("--native-steps", type=int, default=None)
+    ap.add_argument("--solver", default="euler", choices=["euler", "midpoint"])
+    ap.add_argument("--guidance-mode", default="full", choices=["full", "interval", "adaptive"])
+    ap.add_argument("--interval", type=float, nargs=2, default=(0.10, 0.70))
+    ap.add_argument("--adaptive", type=float, nargs=3, default=(0.015, 4, 2),
+                    help="threshold, warm-up steps, patience")
+    ap.add_argument("--cache", action="store_true", help="block-residual cache with its default settings")
     args = ap.parse_args()
     if args.traffic_probe:
         traffic_probe()
@@ -178,6 +213,10 @@ def main():
         sys.exit(2)
 
     s = synth.workload(args.workload)
+    nondefault = (args.schedule != "uniform" or args.solver != "euler" or args.guidance_mode != "full"
+                  or args.cache)
+    if nondefault:   # the per-kernel work model assumes every row at every step
+        args.no_kernel_timing = True
     t0 = time.perf_counter()
     W, I = synth.make_weights(s), synth.make_inputs(s)
     log(f"[bench] {s.name}: inputs drawn in {time.perf_counter() - t0:.1f} s")
@@ -189,13 +228,35 @@ def main():
     import torch
     import flow_matching_tts_amd as F
     torch.cuda.set_device(0)
-    smp = F.Sampler(F.config_from_shape(s), W)
+    per_eval = 2 if args.solver == "midpoint" else 1
+    smp = F.Sampler(F.config_from_shape(s, max_steps=per_eval * s.n_steps), W)
     x0 = torch.from_numpy(I["x0"]).cuda()
     cond = torch.from_numpy(I["cond"]).cuda()
     spk = None if I["spk"] is None else torch.from_numpy(I["spk"]).cuda()
     mask = None if I["mask"] is None else torch.from_numpy(I["mask"]).cuda()
     out = torch.empty_like(x0)
-    run = lambda: smp.sample(x0, cond, mask=mask, spk=spk, n_steps=s.n_steps, guidance=s.guidance, out=out)
+    guided = torch.zeros(s.n_requests, dtype=torch.int32, device="cuda")
+    hits = torch.zeros(1, dtype=torch.int32, device="cuda")
+    options = dict(schedule=args.schedule, native_steps=args.native_steps, solver=args.solver,
+                   guidance_mode=args.guidance_mode, interval=tuple(args.interval),
+                   adaptive=(args.adaptive[0], int(args.adaptive[1]), int(args.adaptive[2])),
+                   cache={} if args.cache else None)
+    eager = lambda: smp.sample(x0, cond, mask=mask, spk=spk, n_steps=s.n_steps, guidance=s.guidance, out=out,
+                               guided_evals=guided, cache_hits=hits, **options)
+    run = eager
+    if args.graph:
+        # the call synchronises nothing and allocates nothing, so one call can be
+        # captured whole and replayed on fixed buffers
+        eager()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        stream = torch.cuda.Stream()
+        stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(graph, stream=stream):
+                eager()
+        torch.cuda.current_stream().wait_stream(stream)
+        run = graph.replay
 
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -217,8 +278,16 @@ def main():
     ms = e0.elapsed_time(e1) / args.steps
     log(f"[bench] {args.steps} timed steps: {ms:.3f} ms per sampling call")
 
+    torch.cuda.synchronize()
+    guided_evals = guided.cpu().tolist()
+    cache_hits = int(hits.cpu()[0])
     lengths = I["lengths"]
     rows = s.n_rows
+    # estimator row-evaluations actually run: all rows at each evaluation, except the
+    # unconditional rows of unguided evaluations and the evaluations cached whole
+    n_eval = per_eval * s.n_steps
+    row_evals = s.n_requests * n_eval + (s.n_branches - 1) * sum(guided_evals) if s.n_branches > 1 \
+        else s.n_requests * n_eval
     evals_s = rows * s.n_steps / (ms / 1e3)
     valid_frames = float(np.sum(np.minimum(lengths, s.n_frames)))
     model = work_model(s, lengths)
@@ -228,7 +297,7 @@ def main():
         # per-class kernel time: one instrumented call per class (events around each launch)
         for cls, (work, launches) in model.items():
             smp.profile_enable(cls, launches + 8)
-            run()
+            eager()
             tot, n, dropped = smp.profile_read()
             smp.profile_disable()
             kernels[cls] = {"ms_per_sample": tot, "launches": n, "mean_us": 1e3 * tot / max(n, 1)}
@@ -237,7 +306,7 @@ def main():
         work, launches = model[dom]
         smp.profile_enable(dom, launches * args.steps + 8)
         for _ in range(args.steps):
-            run()
+            eager()
         tot, n, dropped = smp.profile_read()
         smp.profile_disable()
         mean_s = tot / 1e3 / n
@@ -276,7 +345,9 @@ def main():
         "config": {"workload": s.name, "requests": s.n_requests, "branches": s.n_branches, "rows": rows,
                    "frames": s.n_frames, "layers": s.n_layers, "d_model": s.d_model,
                    "heads": s.n_heads, "ffn": s.ffn_dim, "latent": s.latent_dim,
-                   "euler_steps": s.n_steps, "guidance": list(s.guidance)},
+                   "euler_steps": s.n_steps, "guidance": list(s.guidance), "launch": "graph" if args.graph else "eager",
+                   "sampler": {k: (list(v) if isinstance(v, tuple) else v) for k, v in options.items()}},
+        "row_evaluations_run": row_evals, "guided_evaluations_per_request": guided_evals, "cache_hits": cache_hits,
         "latent_frame_steps_per_s": valid_frames * s.n_steps / (ms / 1e3),
         "generated_frames_per_s": valid_frames / (ms / 1e3),
         "gemm_attn_frac_bf16_peak": gemm_attn_frac,
