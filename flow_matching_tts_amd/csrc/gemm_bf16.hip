@@ -314,10 +314,13 @@ __device__ __forceinline__ void read_frags64(Frags64<C>& f, const bf16* as, cons
     }
 }
 
+// kchunk > 0: split-K. Block b computes the partial product over K-slice b / (tm tn)
+// ([kchunk * slice, kchunk * (slice + 1))) of tile b % (tm tn), written as fp32 to
+// ep.out + slice * ep.ldo * M (the epilogue must be EPI_F32 with no bias).
 template <typename C, int EPI>
 __global__ void __launch_bounds__(C::NT)
 gemm_pp64_kernel(const bf16* __restrict__ A, int lda, const bf16* __restrict__ W, int ldw,
-                 int M, int N, int K, int tm, int tn, EpiParams ep) {
+                 int M, int N, int K, int tm, int tn, EpiParams ep, int kchunk) {
     static_assert(C::WGM == 2 && C::WGN == 4, "two groups of four waves");
     constexpr int SLOT = (C::BM + C::BN) * BK64;                // bf16 elements
     // group 0's waves load A (64 rows each), group 1's waves W (each the 64 rows of
@@ -333,15 +336,24 @@ gemm_pp64_kernel(const bf16* __restrict__ A, int lda, const bf16* __restrict__ W
     const int li = lane & 31, lh = lane >> 5;
     // the group decides control flow around barriers: make it provably wave-uniform
     const int grp = __builtin_amdgcn_readfirstlane(wave) / C::WGN, wn = wave % C::WGN;
+    int bid = blockIdx.x;
+    long long koff = 0;
+    if (kchunk > 0) {               // split-K: this block's K-slice and partial-sum plane
+        const int slice = bid / (tm * tn);
+        bid -= slice * tm * tn;
+        koff = (long long)slice * kchunk;
+        K = min(kchunk, K - (int)koff);
+        ep.out = (float*)ep.out + (long long)slice * M * ep.ldo;
+    }
     int mt, nt;
-    tile_of(blockIdx.x, tm * tn, tm, tn, mt, nt);
+    tile_of(bid, tm * tn, tm, tn, mt, nt);
     const int m0 = mt * C::BM, n0 = nt * C::BN;
     if (ep.m_dev) {
         M = min(M, *ep.m_dev);
         if (m0 >= M) return;   // whole block, before any barrier
     }
-    const __amdgpu_buffer_rsrc_t ra = rsrc_of(A, (long long)M * lda * 2);
-    const __amdgpu_buffer_rsrc_t rw = rsrc_of(W, (long long)N * ldw * 2);
+    const __amdgpu_buffer_rsrc_t ra = rsrc_of(A + koff, ((long long)M * lda - koff) * 2);
+    const __amdgpu_buffer_rsrc_t rw = rsrc_of(W + koff, ((long long)N * ldw - koff) * 2);
     const int nk = (K + BK64 - 1) / BK64;
 
     f32x16 acc[C::TM][C::TN];
@@ -448,9 +460,12 @@ gemm_pp64_kernel(const bf16* __restrict__ A, int lda, const bf16* __restrict__ W
     }
 }
 
+using PP = PCfg<256, 256, 2, 4>;   // 8 waves in two groups of four, 128x64 per wave
+using PP128 = PCfg<128, 128, 2, 4>;   // the same schedule on 128x128 tiles, 64x32 per wave
+
 template <typename C, int EPI>
 void launch_pp64(const bf16* A, int lda, const bf16* W, int ldw, int M, int N, int K,
-                 const EpiParams& ep, hipStream_t s) {
+                 const EpiParams& ep, hipStream_t s, int splits = 1, int kchunk = 0) {
     const int tn = (N + C::BN - 1) / C::BN, tm = (M + C::BM - 1) / C::BM;
     constexpr int LDS = 2 * (C::BM + C::BN) * BK64 * 2;
     static_assert(LDS >= C::NW * EPI_WAVE_FLOATS * 4, "epilogue staging fits in the ring");
@@ -459,10 +474,41 @@ void launch_pp64(const bf16* A, int lda, const bf16* W, int ldw, int M, int N, i
                                    hipFuncAttributeMaxDynamicSharedMemorySize, LDS) == hipSuccess;
     }();
     (void)attr;
-    gemm_pp64_kernel<C, EPI><<<tm * tn, C::NT, LDS, s>>>(A, lda, W, ldw, M, N, K, tm, tn, ep);
+    gemm_pp64_kernel<C, EPI><<<tm * tn * splits, C::NT, LDS, s>>>(A, lda, W, ldw, M, N, K, tm, tn, ep, kchunk);
 }
 
-using PP = PCfg<256, 256, 2, 4>;   // 8 waves in two groups of four, 128x64 per wave
+// Split-K reduction: out tile = epilogue(sum over the slices' fp32 partial products),
+// four columns per thread, slices summed in order (the result does not depend on
+// how the blocks ran). Rows past the device row count are skipped.
+template <int EPI>
+__global__ void __launch_bounds__(256)
+splitk_reduce_kernel(const float* __restrict__ part, int splits, int M, int N, EpiParams ep) {
+    const long long plane = (long long)M * N;     // one slice's partial products, [M, N]
+    if (ep.m_dev) M = min(M, *ep.m_dev);
+    const int n4 = N / 4;
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (long long)M * n4) return;
+    const int m = (int)(i / n4), n = (int)(i - (long long)m * n4) * 4;
+    f32x4 v = *(const f32x4*)(part + (long long)m * N + n);
+    for (int sl = 1; sl < splits; ++sl) v += *(const f32x4*)(part + sl * plane + (long long)m * N + n);
+    epi_store_vec4<EPI>(ep, m, n, v);
+}
+
+// The partial products of a split-K GEMM (EPI_F32, no bias, fp32 planes in the
+// caller's split workspace), then the reduction with the real epilogue.
+template <int EPI>
+void launch_splitk(const bf16* A, int lda, const bf16* W, int ldw, int M, int N, int K, const EpiParams& ep,
+                   int splits, hipStream_t s) {
+    const int kchunk = (K / splits + BK64 - 1) / BK64 * BK64;
+    EpiParams pe;
+    pe.out = ep.split_ws;
+    pe.ldo = N;
+    pe.m_dev = ep.m_dev;
+    launch_pp64<PP128, EPI_F32>(A, lda, W, ldw, M, N, K, pe, s, splits, kchunk);
+    const long long n = (long long)M * (N / 4);
+    splitk_reduce_kernel<EPI><<<(int)((n + 255) / 256), 256, 0, s>>>(ep.split_ws, splits, M, N, ep);
+}
+
 
 // tile configurations (index = the `tile` argument; 0 = automatic)
 using C1 = Cfg<128, 128, 32, 2, 2>;     // 4 waves, 64x64 per wave
@@ -478,16 +524,30 @@ void launch_epi(int tile, const AT* A, int lda, const bf16* W, int ldw, int M, i
     } else {
         if (tile == 0) {
             // the largest tile that still gives about one tile per CU or more; 256x256
-            // tiles run the K-64 ping-pong kernel, unless N and K are both small (then
-            // 128x128 tiles, whose fixed cost is lower, win)
+            // and 128x128 tiles run the K-64 ping-pong kernel, unless N and K are both
+            // small (then the register-staged 128x128 kernel, whose fixed cost is
+            // lower, wins)
             const long long big = (long long)((M + 255) / 256) * ((N + 255) / 256);
             const long long mid = (long long)((M + 127) / 128) * ((N + 127) / 128);
-            tile = big >= 192 ? (N >= 1024 || K >= 1024 ? 14 : 1) : mid >= 160 ? 6 : 10;
+            tile = big >= 192 ? (N >= 1024 || K >= 1024 ? 14 : 1) : mid >= 160 ? 15 : 10;
+            // few 128x128 tiles and a long K: split K over 128x128 tiles when the
+            // caller provides room for the partial products (gated-residual and plain
+            // fp32 epilogues, which take four columns at a time). The slice count
+            // depends on K alone, so a row's result does not depend on how many other
+            // rows share the call while the batch stays in this regime.
+            if (tile == 10 && (EPI == EPI_GATED || EPI == EPI_F32) && ep.split_ws != nullptr && N % 4 == 0) {
+                const int splits = (int)std::min(4, K / 512);
+                if (splits >= 2 && (long long)M * N * splits <= ep.split_ws_floats) {
+                    launch_splitk<EPI>(A, lda, W, ldw, M, N, K, ep, splits, s);
+                    return;
+                }
+            }
         }
         switch (tile) {
             case 6: launch_cfg<C6, AT, EPI>(A, lda, W, ldw, M, N, K, ep, s); break;
             case 10: launch_cfg<C10, AT, EPI>(A, lda, W, ldw, M, N, K, ep, s); break;
             case 14: launch_pp64<PP, EPI>(A, lda, W, ldw, M, N, K, ep, s); break;
+            case 15: launch_pp64<PP128, EPI>(A, lda, W, ldw, M, N, K, ep, s); break;
             default: launch_cfg<C1, AT, EPI>(A, lda, W, ldw, M, N, K, ep, s); break;
         }
     }

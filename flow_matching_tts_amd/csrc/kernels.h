@@ -43,6 +43,10 @@ struct EpiParams {
     // optional device row count (at most M): the grid is sized for M and the
     // tiles past *m_dev exit at once
     const int32_t* m_dev = nullptr;
+    // optional room for split-K partial products (fp32): a bf16 GEMM with few tiles and
+    // a long K may then split K (the library picks the split; M * N * splits floats)
+    float* split_ws = nullptr;
+    long long split_ws_floats = 0;
 };
 
 // bf16 MFMA GEMM, A bf16 or f32 (rounded to bf16 while staging), W bf16 [N, K].

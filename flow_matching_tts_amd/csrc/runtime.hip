@@ -46,6 +46,7 @@ cfm_status fail(cfm_status s, const char* fmt, ...) {
 }
 
 constexpr long long kMaxOperandBytes = (1LL << 31) - 256;
+constexpr size_t kSplitKTokens = 4096;   // batches up to this many tokens may split K
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 inline long long round8(long long v) { return (v + 7) / 8 * 8; }
@@ -187,7 +188,7 @@ Slot find(const Manifest& m, const char* name, long long col0 = 0) {
 
 struct Layout {   // workspace regions, byte offsets
     size_t h, act, big, vt, v, cproj, temb, tpre, ct, spkproj, cvec, mod, kvlen, kvalid, tfull, rowoff, tokrow,
-        xmid, lanes, probe, resid, cstate, cparts, total;
+        xmid, lanes, probe, resid, cstate, cparts, splitk, total;
 };
 
 inline long long round64(long long v) { return (v + 63) / 64 * 64; }
@@ -232,6 +233,9 @@ Layout plan_workspace(const cfm_config& c) {
     L.resid = take(N * TT * d * 4);                      // ... and the saved middle-block residual
     L.cstate = take(8 * 4);
     L.cparts = take(kCacheParts * 2 * 4);
+    // split-K partial products of the gated-residual GEMMs (N = d) of small batches:
+    // up to 4 fp32 planes of [tokens, d]; large batches never split
+    L.splitk = take(c.dtype == CFM_BF16 && N * TT <= kSplitKTokens ? 4 * N * TT * d * 4 : 0);
     L.total = off;
     return L;
 }
@@ -567,6 +571,8 @@ cfm_status cfm_sample_ex(cfm_ctx* c, const float* x0, const float* cond, const f
     float* mod = wsp<float>(c, ly.mod);
     float* xmid = wsp<float>(c, ly.xmid);
     float* probe = wsp<float>(c, ly.probe);
+    float* splitk = ly.splitk < ly.total && bf ? wsp<float>(c, ly.splitk) : nullptr;
+    const long long splitk_floats = splitk ? (long long)((ly.total - ly.splitk) / 4) : 0;
     float* resid = wsp<float>(c, ly.resid);
     int32_t* cstate = wsp<int32_t>(c, ly.cstate);
     float* cparts = wsp<float>(c, ly.cparts);
@@ -717,6 +723,7 @@ cfm_status cfm_sample_ex(cfm_ctx* c, const float* x0, const float* cond, const f
             });
             EpiParams e2; e2.bias = wp<float>(c, W.projb); e2.out = h; e2.ldo = d; e2.gate = rowmod(ml + 2 * d, T);
             e2.m_dev = ntok_l;
+            e2.split_ws = splitk; e2.split_ws_floats = splitk_floats;
             gemm(CFM_K_GEMM_PROJ, false, act, d, W.projw, (int)NTk, d, d, EPI_GATED, e2);
             ln.shift = rowmod(ml + 3 * d, T); ln.scale = rowmod(ml + 4 * d, T);
             timed(c, CFM_K_ADALN, s, [&] { launch_adaln(ln, s); });
@@ -724,6 +731,7 @@ cfm_status cfm_sample_ex(cfm_ctx* c, const float* x0, const float* cond, const f
             gemm(CFM_K_GEMM_FC1, false, act, d, W.fc1w, (int)NTk, f, d, EPI_GELU_ACT, e3);
             EpiParams e4; e4.bias = wp<float>(c, W.fc2b); e4.out = h; e4.ldo = d; e4.gate = rowmod(ml + 5 * d, T);
             e4.m_dev = ntok_l;
+            e4.split_ws = splitk; e4.split_ws_floats = splitk_floats;
             gemm(CFM_K_GEMM_FC2, false, big, f, W.fc2w, (int)NTk, d, f, EPI_GATED, e4);
             if (caching && l == cb - 1)   // computed: save the residual; hit: add the saved one
                 timed(c, CFM_K_HOISTED, s, [&] { launch_cache_apply(h, resid, probe, d, tk, cstate, s); });
@@ -835,7 +843,7 @@ cfm_status cfm_gemm_bf16(const void* A, int a_is_f32, int lda, const void* W, in
                          const float* bias, int M, int N, int K, int epilogue,
                          const float* gate, void* C, int ldc, int tile, void* stream) {
     if (M < 0 || N < 0 || K < 0) return fail(CFM_E_VALUE, "negative size");
-    if (!(tile == 0 || tile == 1 || tile == 6 || tile == 10 || tile == 14) || (tile > 1 && a_is_f32))
+    if (!(tile == 0 || tile == 1 || tile == 6 || tile == 10 || tile == 14 || tile == 15) || (tile > 1 && a_is_f32))
         return fail(CFM_E_VALUE, "tile %d", tile);
     if (epilogue < 0 || epilogue > 3) return fail(CFM_E_VALUE, "epilogue %d", epilogue);
     if (M == 0 || N == 0) return CFM_OK;

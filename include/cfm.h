@@ -295,7 +295,8 @@ cfm_status cfm_cfg_euler(const float* v, const float* w, int nb, float dt, const
  * or 4 (fp32 A); ldw >= K rounded up to 8 with zero padding.
  * tile: 0 = chosen from the problem size (what cfm_sample uses); 1 = 128x128
  * tiles, 6 = 128x128 with a K stage of 64, 10 = 64x64, 14 = 256x256 with two
- * wave groups alternating loads and MFMAs (K stage 64). Any other value returns
+ * wave groups alternating loads and MFMAs (K stage 64), 15 = as 14 on 128x128
+ * tiles. Any other value returns
  * CFM_E_VALUE, as does a tile other than 0 or 1 with an fp32 A operand. The GELU
  * of epilogue 2 is evaluated with an erfc approximation of relative error below
  * 1e-5 (bf16 rounding: 2^-9).

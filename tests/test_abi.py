@@ -191,7 +191,7 @@ def test_gemm_entry_rejects_misaligned_outputs(lib):
     assert ok(C=c + 8) == 2
     assert ok(bias=c + 4) == 2
     assert ok(epi=3, gate=c + 4) == 2
-    assert ok(tile=2) == 4 and ok(tile=13) == 4 and ok(tile=15) == 4   # tiles the library does not have
+    assert ok(tile=2) == 4 and ok(tile=13) == 4 and ok(tile=16) == 4   # tiles the library does not have
 
 
 def test_binding_rejects_bad_shapes_before_any_launch():

@@ -86,7 +86,7 @@ def _gemm_ref(A, W, bias, epi, gate=None, c0=None):
 @pytest.mark.parametrize("M,N,K", [(300, 200, 136), (128, 128, 64), (1, 3, 8), (1000, 100, 1024), (257, 3072, 1024),
                                    (520, 600, 2048)])
 @pytest.mark.parametrize("epi", [0, 1, 2, 3])
-@pytest.mark.parametrize("tile", [0, 1, 6, 10, 14])
+@pytest.mark.parametrize("tile", [0, 1, 6, 10, 14, 15])
 def test_gemm_bf16_epilogues(M, N, K, epi, tile):
     import flow_matching_tts_amd as F
     rng = np.random.default_rng(M * 7 + N + K + epi)

@@ -113,39 +113,48 @@ def test_full_workload_matches_stored_oracle(name):
     np.testing.assert_array_equal(got[~_valid(I, s)], I["x0"][~_valid(I, s)])
 
 
+def _stacked_branch_inputs(I, branches):
+    """One-branch inputs whose requests are the given branch inputs stacked in branch
+    order: request b * R + r sees branch b's inputs of request r. A one-branch run on
+    them lays every row where the CFG run lays it, so both runs have the same row
+    count and kernel configuration and the comparison below can be tight."""
+    cat = lambda k: np.concatenate([b[k] for b in branches]) if branches[0][k] is not None else None
+    return {"x0": np.concatenate([I["x0"]] * len(branches)), "cond": cat("cond"), "spk": cat("spk"),
+            "mask": None if I["mask"] is None else np.concatenate([I["mask"]] * len(branches)),
+            "lengths": None}
+
+
 def test_guidance_one_equals_conditional_branch_and_zero_the_unconditional():
     s = reduced("mel_dit")
     W, I = synth.make_weights(s, 301), synth.make_inputs(s, 302)
-    s1 = s.replace(n_branches=1, guidance=())
+    R = s.n_requests
+    s1 = s.replace(n_branches=1, guidance=(), n_requests=2 * R)
+    uncond = dict(I, cond=np.zeros_like(I["cond"]))
+    both, _ = run_sampler(s1, W, _stacked_branch_inputs(I, [uncond, I]))   # rows: uncond, cond
     full1, _ = run_sampler(s, W, I, guidance=(1.0,))
-    cond_only, _ = run_sampler(s1, W, I)
-    np.testing.assert_allclose(full1, cond_only, rtol=0, atol=1e-6)
+    np.testing.assert_allclose(full1, both[R:], rtol=0, atol=1e-6)
     full0, _ = run_sampler(s, W, I, guidance=(0.0,))
-    I0 = dict(I, cond=np.zeros_like(I["cond"]))
-    uncond_only, _ = run_sampler(s1, W, I0)
-    np.testing.assert_allclose(full0, uncond_only, rtol=0, atol=1e-6)
+    np.testing.assert_allclose(full0, both[:R], rtol=0, atol=1e-6)
 
 
 def test_three_branch_reductions_on_gpu():
     """Three-branch guidance v_u + s_t (v_t - v_u) + s_s (v_ts - v_t): (1, 1) gives the
     text+speaker branch alone, (1, 0) the text branch alone, (0, 0) the unconditional
-    branch alone. A one-branch run carries the speaker vector; the text branch is that
-    run with the speaker vector zeroed, the unconditional one with the text condition
+    branch alone. A one-branch row carries the speaker vector; the text branch is that
+    row with the speaker vector zeroed, the unconditional one with the text condition
     zeroed as well."""
     s = reduced("multicond_rf")
     W, I = synth.make_weights(s, 311), synth.make_inputs(s, 312)
-    s1 = s.replace(n_branches=1, guidance=())
-    ts_only, smp1 = run_sampler(s1, W, I)
-    both_one, smp3 = run_sampler(s, W, I, guidance=(1.0, 1.0))
-    np.testing.assert_allclose(both_one, ts_only, rtol=0, atol=1e-6)
-    I_t = dict(I, spk=np.zeros_like(I["spk"]))
-    t_only, _ = run_sampler(s1, W, I_t, sampler=smp1)
-    text_one, _ = run_sampler(s, W, I, guidance=(1.0, 0.0), sampler=smp3)
-    np.testing.assert_allclose(text_one, t_only, rtol=0, atol=1e-6)
-    I_u = dict(I_t, cond=np.zeros_like(I["cond"]))
-    u_only, _ = run_sampler(s1, W, I_u, sampler=smp1)
-    none, _ = run_sampler(s, W, I, guidance=(0.0, 0.0), sampler=smp3)
-    np.testing.assert_allclose(none, u_only, rtol=0, atol=1e-6)
+    R = s.n_requests
+    s1 = s.replace(n_branches=1, guidance=(), n_requests=3 * R)
+    text = dict(I, spk=np.zeros_like(I["spk"]))
+    uncond = dict(text, cond=np.zeros_like(I["cond"]))
+    alone, _ = run_sampler(s1, W, _stacked_branch_inputs(I, [uncond, text, I]))
+    u_only, t_only, ts_only = alone[:R], alone[R:2 * R], alone[2 * R:]
+    smp3 = None
+    for scales, want in (((1.0, 1.0), ts_only), ((1.0, 0.0), t_only), ((0.0, 0.0), u_only)):
+        got, smp3 = run_sampler(s, W, I, guidance=scales, sampler=smp3)
+        np.testing.assert_allclose(got, want, rtol=0, atol=1e-6, err_msg=str(scales))
     assert np.abs(t_only - ts_only).max() > 1e-3 and np.abs(u_only - t_only).max() > 1e-3
 
 
