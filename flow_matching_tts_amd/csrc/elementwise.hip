@@ -418,13 +418,15 @@ __global__ void pack_rows_kernel(const int32_t* row_off, int N, int NTmax, int32
 }
 
 __global__ void assemble_cvec_kernel(const float* ct, const float* bs, const float* spkproj,
-                                     int nc, int d, float* cvec) {
+                                     int nc, int d, float* cvec, bf16* silu_bf16) {
     const int n = blockIdx.x * blockDim.x + threadIdx.x;
     const int ci = blockIdx.y, k = blockIdx.z;
     if (n >= d) return;
     float v = ct[(long long)k * d + n];
     if (bs != nullptr) v += ci == 0 ? bs[n] : spkproj[(long long)(ci - 1) * d + n];
-    cvec[((long long)k * nc + ci) * d + n] = v;
+    const long long o = ((long long)k * nc + ci) * d + n;
+    if (silu_bf16) silu_bf16[o] = (bf16)silu(v);
+    else cvec[o] = v;
 }
 
 __global__ void prefix_init_kernel(const float* cproj, const float* bias, int R, int cond_branch0,
@@ -523,9 +525,9 @@ void launch_pack_rows(const int32_t* kv_len, const int32_t* lane_off, int R, int
 }
 
 void launch_assemble_cvec(const float* ct, const float* bs, const float* spkproj, int S, int nc,
-                          int d, float* cvec, hipStream_t s) {
+                          int d, float* cvec, hipStream_t s, bf16* silu_bf16) {
     if (S <= 0) return;
-    assemble_cvec_kernel<<<dim3((d + 255) / 256, nc, S), 256, 0, s>>>(ct, bs, spkproj, nc, d, cvec);
+    assemble_cvec_kernel<<<dim3((d + 255) / 256, nc, S), 256, 0, s>>>(ct, bs, spkproj, nc, d, cvec, silu_bf16);
 }
 
 void launch_prefix_init(const float* cproj, const float* bias, int R, int nb, int cond_branch0,

@@ -161,9 +161,11 @@ void launch_key_prep(const uint8_t* mask, int mask_stride, const int32_t* kv_len
 // past the end, up to NTmax).
 void launch_pack_rows(const int32_t* kv_len, const int32_t* lane_off, int R, int nb, int NTmax, int32_t* row_off,
                       int32_t* tok_row, hipStream_t s);
-// cvec[(k*nc + ci), :] = ct[k, :] + (spk ? (ci == 0 ? bs : spkproj[ci-1]) : 0)
+// cvec[(k*nc + ci), :] = ct[k, :] + (spk ? (ci == 0 ? bs : spkproj[ci-1]) : 0); with
+// silu_bf16 set, silu of that vector rounded to bf16 goes there instead (the A operand
+// of the modulation GEMM on matrix cores)
 void launch_assemble_cvec(const float* ct, const float* bs, const float* spkproj, int S, int nc,
-                          int d, float* cvec, hipStream_t s);
+                          int d, float* cvec, hipStream_t s, bf16* silu_bf16 = nullptr);
 // prefix tokens of every branch row: h[(b*R + r)*T + p] = b >= cond_branch0 ? cproj[r*P + p] : bias
 void launch_prefix_init(const float* cproj, const float* bias, int R, int nb, int cond_branch0,
                         int P, int T, int d, float* h, hipStream_t s);

@@ -631,10 +631,23 @@ cfm_status cfm_sample_ex(cfm_ctx* c, const float* x0, const float* cond, const f
     hoisted(false, temb, g.t_freq_dim, c->t1w, c->t1b, n_eval, d, g.t_freq_dim, tpre, d);
     hoisted(true, tpre, d, c->t2w, c->t2b, n_eval, d, d, ct, d);
     if (g.spk_dim > 0) hoisted(false, spk, g.spk_dim, c->spkw, c->spkb, R, d, g.spk_dim, spkproj, d);
+    // the modulation vectors of every evaluation, layer and conditioning vector: one
+    // GEMM over the stacked adaLN weights (bf16 sampler: silu(c) rounded to bf16 as
+    // the A operand on matrix cores, like every other GEMM operand of that path)
+    bf16* cvec_silu = bf ? (bf16*)cvec : nullptr;
     timed(c, CFM_K_HOISTED, s, [&] {
-        launch_assemble_cvec(ct, g.spk_dim > 0 ? wp<float>(c, c->spkb) : nullptr, spkproj, n_eval, nc, d, cvec, s);
+        launch_assemble_cvec(ct, g.spk_dim > 0 ? wp<float>(c, c->spkb) : nullptr, spkproj, n_eval, nc, d, cvec, s,
+                             cvec_silu);
     });
-    hoisted(true, cvec, d, c->adaw, c->adab, n_eval * nc, (int)ML, d, mod, ML);
+    if (bf) {
+        EpiParams ep;
+        ep.bias = wp<float>(c, c->adab);
+        ep.out = mod;
+        ep.ldo = ML;
+        gemm(CFM_K_HOISTED, false, cvec_silu, d, c->adaw, n_eval * nc, (int)ML, d, EPI_F32, ep);
+    } else {
+        hoisted(true, cvec, d, c->adaw, c->adab, n_eval * nc, (int)ML, d, mod, ML);
+    }
     {
         EpiParams ep;
         ep.bias = wp<float>(c, c->inb);
