@@ -46,9 +46,14 @@ class CfmShape:
     """Sizes of one sampling workload.
 
     ``cond_mode`` is "channel" (a per-frame condition of ``cond_dim`` channels
-    concatenated after the latent channels of every generated frame) or
-    "prefix" (``n_prefix`` condition frames of the latent width placed before
-    the generated frames in the sequence).
+    concatenated after the latent channels of every generated frame), "prefix"
+    (``n_prefix`` condition frames of the latent width placed before the
+    generated frames in the sequence) or "cross" (``n_prefix`` context tokens of
+    ``cond_dim`` channels that every block reads through cross-attention).
+
+    Block variants: ``norm`` "layer" or "rms"; ``mlp`` "gelu" (FC1 of ffn_dim
+    rows) or "swiglu" (one fused gate-up FC1 of 2 ffn_dim rows, gate rows first);
+    ``rope`` rotates the self-attention queries and keys by token position.
     """
     name: str
     n_layers: int
@@ -69,7 +74,11 @@ class CfmShape:
     varlen: Optional[Tuple[int, int]] = None   # inclusive [lo, hi] frame lengths
     t_freq_dim: int = 256
     weight_std: float = 0.02
-    index: int = -1                 # position in WORKLOAD_ORDER (seed offset)
+    index: int = -1                 # seed offset (position in WORKLOAD_ORDER for the five main cases)
+    norm: str = "layer"             # "layer" | "rms"
+    mlp: str = "gelu"               # "gelu" | "swiglu"
+    rope: bool = False
+    rope_base: float = 10000.0
 
     @property
     def head_dim(self) -> int:
@@ -82,7 +91,7 @@ class CfmShape:
 
     @property
     def cond_frames(self) -> int:
-        return self.n_prefix if self.cond_mode == "prefix" else self.n_frames
+        return self.n_prefix if self.cond_mode in ("prefix", "cross") else self.n_frames
 
     @property
     def in_dim(self) -> int:
@@ -134,6 +143,30 @@ WORKLOADS: Dict[str, CfmShape] = {
         latent_dim=32, cond_dim=512, cond_mode="channel", n_prefix=0, spk_dim=256,
         n_branches=3, dtype="bf16", n_requests=16, n_frames=750, n_steps=40,
         guidance=(3.0, 1.5), index=4),
+    # Block variants (parity and measurement cases beside the five main ones).
+    # LocDiT decode tail with RMSNorm, a fused gate-up SwiGLU MLP and rotary
+    # positions over the prefix + patch tokens: 64 requests x CFG, 4 + 4 tokens.
+    "locdit_swiglu": CfmShape(
+        name="locdit_swiglu", n_layers=4, d_model=1024, n_heads=16, ffn_dim=2048,
+        latent_dim=64, cond_dim=64, cond_mode="prefix", n_prefix=4, spk_dim=0,
+        n_branches=2, dtype="bf16", n_requests=64, n_frames=4, n_steps=10,
+        guidance=(2.0,), index=5, norm="rms", mlp="swiglu", rope=True),
+    # Cross-attention DiT: 200 context tokens of 512 channels read by every block
+    # through cross-attention (keys/values computed once per call), rotary
+    # self-attention over 600 frames of latent 64, 8 requests x 3 branches
+    # (uncond, text, text+speaker), 12 layers, d=1024, FFN 4096, 16 steps.
+    "cross_dit": CfmShape(
+        name="cross_dit", n_layers=12, d_model=1024, n_heads=16, ffn_dim=4096,
+        latent_dim=64, cond_dim=512, cond_mode="cross", n_prefix=200, spk_dim=128,
+        n_branches=3, dtype="bf16", n_requests=8, n_frames=600, n_steps=16,
+        guidance=(2.0, 1.5), varlen=(300, 600), index=6, rope=True),
+    # Tiny fp32 case with every variant on: cross-attention to 12 context tokens,
+    # RMSNorm, SwiGLU, rotary positions; 2 requests with CFG, 24 frames.
+    "tiny_f32_variants": CfmShape(
+        name="tiny_f32_variants", n_layers=2, d_model=64, n_heads=4, ffn_dim=96,
+        latent_dim=16, cond_dim=20, cond_mode="cross", n_prefix=12, spk_dim=0,
+        n_branches=2, dtype="f32", n_requests=2, n_frames=24, n_steps=4,
+        guidance=(2.0,), index=7, norm="rms", mlp="swiglu", rope=True),
 }
 WORKLOAD_ORDER: List[str] = ["tiny_f32", "locdit_tail", "mel_dit", "varlen_masked", "multicond_rf"]
 
@@ -155,15 +188,22 @@ def weight_specs(s: CfmShape) -> List[Tuple[str, Tuple[int, ...]]]:
     if s.spk_dim > 0:
         specs += [("spk_proj.weight", (d, s.spk_dim)), ("spk_proj.bias", (d,))]
     specs += [("in_proj.weight", (d, s.in_dim)), ("in_proj.bias", (d,))]
+    f1 = 2 * f if s.mlp == "swiglu" else f      # fused gate-up: gate rows, then up rows
     for l in range(s.n_layers):
         p = f"blocks.{l}."
         specs += [
             (p + "ada.weight", (6 * d, d)), (p + "ada.bias", (6 * d,)),
             (p + "qkv.weight", (3 * d, d)), (p + "qkv.bias", (3 * d,)),
             (p + "proj.weight", (d, d)), (p + "proj.bias", (d,)),
-            (p + "fc1.weight", (f, d)), (p + "fc1.bias", (f,)),
+            (p + "fc1.weight", (f1, d)), (p + "fc1.bias", (f1,)),
             (p + "fc2.weight", (d, f)), (p + "fc2.bias", (d,)),
         ]
+        if s.cond_mode == "cross":
+            specs += [
+                (p + "xattn.q.weight", (d, d)), (p + "xattn.q.bias", (d,)),
+                (p + "xattn.kv.weight", (2 * d, s.cond_dim)), (p + "xattn.kv.bias", (2 * d,)),
+                (p + "xattn.out.weight", (d, d)), (p + "xattn.out.bias", (d,)),
+            ]
     specs += [
         ("final.ada.weight", (2 * d, d)), ("final.ada.bias", (2 * d,)),
         ("final.out.weight", (s.latent_dim, d)), ("final.out.bias", (s.latent_dim,)),
