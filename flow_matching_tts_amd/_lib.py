@@ -16,11 +16,14 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libcfm_mi355x.so")
 
 CFM_F32, CFM_BF16 = 0, 1
-CFM_COND_CHANNEL, CFM_COND_PREFIX = 0, 1
+CFM_COND_CHANNEL, CFM_COND_PREFIX, CFM_COND_CROSS = 0, 1, 2
+NORMS = {"layer": 0, "rms": 1}
+MLPS = {"gelu": 0, "swiglu": 1}
 STATUS = {0: "CFM_OK", 1: "CFM_E_NULL", 2: "CFM_E_SHAPE", 3: "CFM_E_CAPACITY", 4: "CFM_E_VALUE",
           5: "CFM_E_UNSUPPORTED", 6: "CFM_E_WORKSPACE", 7: "CFM_E_HIP"}
 KERNEL_CLASSES = {"gemm_qkv": 0, "gemm_proj": 1, "gemm_fc1": 2, "gemm_fc2": 3, "attention": 4,
-                  "adaln": 5, "cfg_euler": 6, "gemm_in": 7, "gemm_out": 8, "hoisted": 9}
+                  "adaln": 5, "cfg_euler": 6, "gemm_in": 7, "gemm_out": 8, "hoisted": 9,
+                  "xattn": 10, "gemm_xattn": 11}
 
 EXPORTS = ["cfm_weights_bytes", "cfm_workspace_bytes", "cfm_weight_manifest", "cfm_create",
            "cfm_sample", "cfm_sample_ex", "cfm_destroy", "cfm_status_string", "cfm_last_error_detail",
@@ -32,13 +35,13 @@ class cfm_config(C.Structure):
     _fields_ = [(n, C.c_int32) for n in (
         "n_layers", "d_model", "n_heads", "ffn_dim", "latent_dim", "cond_dim", "cond_mode",
         "n_prefix", "spk_dim", "t_freq_dim", "n_branches", "dtype", "max_requests",
-        "max_frames", "max_steps")]
+        "max_frames", "max_steps", "norm", "mlp", "rope")] + [("rope_base", C.c_float)]
 
 
 class cfm_tensor_desc(C.Structure):
     _fields_ = [("name", C.c_char * 48), ("row0", C.c_int64), ("col0", C.c_int64),
                 ("rows", C.c_int64), ("cols", C.c_int64), ("ld", C.c_int64),
-                ("offset", C.c_int64), ("dtype", C.c_int32), ("reserved", C.c_int32)]
+                ("offset", C.c_int64), ("dtype", C.c_int32), ("interleave", C.c_int32)]
 
 
 SCHEDULES = {"uniform": 0, "quadratic": 1, "trailing": 2, "native": 3}
@@ -127,23 +130,26 @@ def check(status: int) -> None:
 
 def make_config(*, n_layers, d_model, n_heads, ffn_dim, latent_dim, cond_dim, cond_mode,
                 n_prefix, spk_dim, n_branches, dtype, max_requests, max_frames, max_steps,
-                t_freq_dim=256) -> cfm_config:
-    cm = {"channel": CFM_COND_CHANNEL, "prefix": CFM_COND_PREFIX}.get(cond_mode, cond_mode)
+                t_freq_dim=256, norm="layer", mlp="gelu", rope=False, rope_base=10000.0) -> cfm_config:
+    cm = {"channel": CFM_COND_CHANNEL, "prefix": CFM_COND_PREFIX, "cross": CFM_COND_CROSS}.get(cond_mode, cond_mode)
     dt = {"f32": CFM_F32, "bf16": CFM_BF16}.get(dtype, dtype)
     return cfm_config(n_layers, d_model, n_heads, ffn_dim, latent_dim, cond_dim, cm, n_prefix,
-                      spk_dim, t_freq_dim, n_branches, dt, max_requests, max_frames, max_steps)
+                      spk_dim, t_freq_dim, n_branches, dt, max_requests, max_frames, max_steps,
+                      NORMS.get(norm, norm), MLPS.get(mlp, mlp), int(bool(rope)), float(rope_base))
 
 
 def config_from_shape(s, *, max_requests: Optional[int] = None, max_frames: Optional[int] = None,
                       max_steps: Optional[int] = None) -> cfm_config:
     """cfm_config of a workload description: any object with the model attributes
     (n_layers, d_model, n_heads, ffn_dim, latent_dim, cond_dim, cond_mode, n_prefix,
-    spk_dim, n_branches, dtype, t_freq_dim) and its n_requests / n_frames / n_steps,
-    which give the capacity unless overridden."""
+    spk_dim, n_branches, dtype, t_freq_dim; optionally norm, mlp, rope, rope_base) and
+    its n_requests / n_frames / n_steps, which give the capacity unless overridden."""
     return make_config(
         n_layers=s.n_layers, d_model=s.d_model, n_heads=s.n_heads, ffn_dim=s.ffn_dim,
         latent_dim=s.latent_dim, cond_dim=s.cond_dim, cond_mode=s.cond_mode, n_prefix=s.n_prefix,
         spk_dim=s.spk_dim, n_branches=s.n_branches, dtype=s.dtype, t_freq_dim=s.t_freq_dim,
+        norm=getattr(s, "norm", "layer"), mlp=getattr(s, "mlp", "gelu"), rope=getattr(s, "rope", False),
+        rope_base=getattr(s, "rope_base", 10000.0),
         max_requests=s.n_requests if max_requests is None else max_requests,
         max_frames=s.n_frames if max_frames is None else max_frames,
         max_steps=s.n_steps if max_steps is None else max_steps)
@@ -165,7 +171,17 @@ def weight_manifest(cfg: cfm_config):
     arr = (cfm_tensor_desc * n)()
     check(0 if lib.cfm_weight_manifest(C.byref(cfg), arr, n) == n else 4)
     return [dict(name=a.name.decode(), row0=a.row0, col0=a.col0, rows=a.rows, cols=a.cols,
-                 ld=a.ld, offset=a.offset, dtype=a.dtype) for a in arr]
+                 ld=a.ld, offset=a.offset, dtype=a.dtype, interleave=a.interleave) for a in arr]
+
+
+def interleave_rows(blk: np.ndarray, k: int) -> np.ndarray:
+    """Row order of a slot with interleave k: groups of k rows of the first half
+    alternate with the matching groups of the second half."""
+    if k <= 0:
+        return blk
+    half = blk.shape[0] // 2
+    a, b = blk[:half].reshape(-1, k, blk.shape[1]), blk[half:].reshape(-1, k, blk.shape[1])
+    return np.stack([a, b], axis=1).reshape(blk.shape)
 
 
 def pack_weights(cfg: cfm_config, weights: Mapping[str, np.ndarray]) -> np.ndarray:
@@ -179,6 +195,8 @@ def pack_weights(cfg: cfm_config, weights: Mapping[str, np.ndarray]) -> np.ndarr
         blk = src[e["row0"]:e["row0"] + e["rows"], e["col0"]:e["col0"] + e["cols"]]
         if blk.shape != (e["rows"], e["cols"]):
             raise ValueError(f"{e['name']}: shape {src.shape} does not cover slot {e}")
+        if e["interleave"]:     # a bias slot is one row: interleave its elements
+            blk = interleave_rows(blk.T, e["interleave"]).T if blk.shape[0] == 1 else interleave_rows(blk, e["interleave"])
         pad = np.zeros((e["rows"], e["ld"]), dtype=np.float32)
         pad[:, :e["cols"]] = blk
         if e["dtype"] == CFM_BF16:
@@ -238,6 +256,8 @@ def check_sample_args(cfg: cfm_config, x0, cond, mask=None, spk=None, out=None, 
     _need("x0", x0, (R, Tx, cfg.latent_dim), torch.float32)
     if cfg.cond_mode == CFM_COND_PREFIX:
         _need("cond", cond, (R, cfg.n_prefix, cfg.latent_dim), torch.float32)
+    elif cfg.cond_mode == CFM_COND_CROSS:
+        _need("cond", cond, (R, cfg.n_prefix, cfg.cond_dim), torch.float32)
     else:
         _need("cond", cond, (R, Tx, cfg.cond_dim), torch.float32)
     _need("mask", mask, (R, Tx), torch.uint8, optional=True)
@@ -392,10 +412,13 @@ def gemm_bf16(A, W, bias=None, *, epilogue: int, out, gate=None, K: Optional[int
     _need("A", A, (M, lda), A.dtype)
     _need("W", W, (N, ldw), torch.bfloat16)
     _need("bias", bias, (N,), torch.float32, optional=True)
-    out_dtype = torch.bfloat16 if epilogue in (1, 2) else torch.float32
+    out_dtype = torch.bfloat16 if epilogue in (1, 2, 4) else torch.float32
     _need("out", out, (M, None), out_dtype)
-    if int(out.shape[1]) < N:
-        raise ValueError(f"out has {int(out.shape[1])} columns, needs at least N={N}")
+    ncols = N // 2 if epilogue == 4 else N
+    if epilogue == 4 and N % 32:
+        raise ValueError(f"the SwiGLU epilogue needs N % 32 == 0, got N={N}")
+    if int(out.shape[1]) < ncols:
+        raise ValueError(f"out has {int(out.shape[1])} columns, needs at least {ncols}")
     if epilogue == 3:
         _need("gate", gate, (N,), torch.float32)
     a_f32 = 1 if A.dtype == torch.float32 else 0

@@ -126,12 +126,16 @@ attn_bf16_kernel(AttnParams p) {
     const int d = p.H * HD;
     const long long ldk = 2LL * d;
     const bf16* qbase = (const bf16*)p.qkv + rbase * ldk + head * HD;
-    const bf16* kbase = qbase + d;
+    // keys: the row's own tokens, or (cross-attention) its Tk context tokens
+    const bool cross = p.kx != nullptr;
+    const int Tk = cross ? p.Tk : T;
+    const long long ldkk = cross ? p.ldkx : ldk;
+    const bf16* kbase = cross ? (const bf16*)p.kx + (long long)row * p.Tk * p.ldkx + head * HD : qbase + d;
     const bf16* vtbase = (const bf16*)p.vt + (long long)(row * p.H + head) * HD * p.Tp;
     const int q = blockIdx.x * QT + wave * 32 + j;
 
     const int rr = row % p.kv_mod;
-    const int kvl = min(p.kv_len[rr], T);
+    const int kvl = min(p.kv_len[rr], Tk);
     const int ntiles = (kvl + KT - 1) / KT;
     const int Tp = p.Tp;
 
@@ -153,7 +157,7 @@ attn_bf16_kernel(AttnParams p) {
     __syncthreads();
 
     // K rows past the key length are out of range: they load as zeros
-    const __amdgpu_buffer_rsrc_t rk = arsrc(kbase, kvl > 0 ? ((long long)(kvl - 1) * ldk + HD) * 2 : 0);
+    const __amdgpu_buffer_rsrc_t rk = arsrc(kbase, kvl > 0 ? ((long long)(kvl - 1) * ldkk + HD) * 2 : 0);
     const __amdgpu_buffer_rsrc_t rv = arsrc(vtbase, (long long)HD * Tp * 2);
     const int lrow = lane / 9, lchunk = lane - 9 * (lane / 9);   // this lane's row / chunk in a load
     auto issue = [&](int it) {
@@ -172,7 +176,7 @@ attn_bf16_kernel(AttnParams p) {
             const unsigned dst = slot + (isk ? 0u : (unsigned)TILE_B) + (unsigned)(gg * GRP * RS);
             if (isk) {
                 const int key = it * KT + r;
-                adma16(rk, ok && key < kvl ? (int)(((long long)key * ldk + lchunk * 8) * 2) : OOB, dst);
+                adma16(rk, ok && key < kvl ? (int)(((long long)key * ldkk + lchunk * 8) * 2) : OOB, dst);
             } else {
                 adma16(rv, ok ? (int)(((long long)r * Tp + it * KT + lchunk * 8) * 2) : OOB, dst);
             }
@@ -383,7 +387,10 @@ attn_short_kernel(AttnParams p) {
     const int d = p.H * HD;
     const long long ldk = 2LL * d;
     const bf16* qbase = (const bf16*)p.qkv + rbase * ldk + head * HD;
-    const bf16* kbase = qbase + d;
+    const bool cross = p.kx != nullptr;        // keys from the context (one tile: Tk <= 64)
+    const int Tk = cross ? p.Tk : T;
+    const long long ldkk = cross ? p.ldkx : ldk;
+    const bf16* kbase = cross ? (const bf16*)p.kx + (long long)row * p.Tk * p.ldkx + head * HD : qbase + d;
     const bf16* vtbase = (const bf16*)p.vt + (long long)(row * p.H + head) * HD * p.Tp;
     const int q = blockIdx.x * QT + wave * 32 + j;
 
@@ -393,7 +400,7 @@ attn_short_kernel(AttnParams p) {
         qf[kk] = q < T ? *(const bf16x8*)(qbase + (long long)q * ldk + kk * 16 + h * 8) : bf16x8{};
 
     const int rr = row % p.kv_mod;
-    const int kvl = min(p.kv_len[rr], T);
+    const int kvl = min(p.kv_len[rr], Tk);
     const uint8_t* kv = p.kvalid + (long long)rr * p.Tp;
     const uint8_t* tfull = p.tile_full + (long long)rr * (p.Tp / KT);
     const float sl2 = 1.4426950408889634f / sqrtf((float)HD);   // 1/sqrt(hd) in base-2 units
@@ -410,7 +417,7 @@ attn_short_kernel(AttnParams p) {
         const bool full = tfull[it] != 0;
         {
             KvStage<NT> st;
-            st.load(kbase, ldk, T - 1, vtbase, p.Tp, kv, it * KT, tid);
+            st.load(kbase, ldkk, Tk - 1, vtbase, p.Tp, kv, it * KT, tid);
             st.store(Ks[cur], Vt[cur], kbias[cur], tid);
         }
         __syncthreads();
@@ -526,8 +533,14 @@ attn_f32_kernel(AttnParams p) {
     const int T = p.T, d = p.H * HD_;
     const long long ld = 3LL * d;
     const float* base = (const float*)p.qkv + (long long)row * T * ld;
+    // key | value rows: the row's own tokens (at column d of its q|k|v rows), or
+    // (cross-attention) its Tk context tokens
+    const bool cross = p.kx != nullptr;
+    const int Tk = cross ? p.Tk : T;
+    const long long ldkv = cross ? p.ldkx : ld;
+    const float* kvb = cross ? (const float*)p.kx + (long long)row * p.Tk * p.ldkx : base + d;
     const int rr = row % p.kv_mod;
-    const int kvl = min(p.kv_len[rr], T);
+    const int kvl = min(p.kv_len[rr], Tk);
     const uint8_t* km = p.key_mask ? p.key_mask + (long long)rr * p.mask_stride : nullptr;
     const float scale = 1.0f / sqrtf((float)HD_);
     const int qc = q < T ? q : T - 1;
@@ -545,8 +558,8 @@ attn_f32_kernel(AttnParams p) {
             const int kr = idx / HD_, e = idx % HD_;
             const int key = k0 + kr;
             const bool ok = key < kvl;
-            Kt[kr][e] = ok ? base[(long long)key * ld + d + head * HD_ + e] : 0.0f;
-            Vs[kr][e] = ok ? base[(long long)key * ld + 2 * d + head * HD_ + e] : 0.0f;
+            Kt[kr][e] = ok ? kvb[(long long)key * ldkv + head * HD_ + e] : 0.0f;
+            Vs[kr][e] = ok ? kvb[(long long)key * ldkv + d + head * HD_ + e] : 0.0f;
         }
         for (int kr = threadIdx.x; kr < FKT; kr += FQ) {
             const int key = k0 + kr;
@@ -597,7 +610,7 @@ bool attention_bf16_fits(long long T) {
 
 void launch_attention_bf16(const AttnParams& p, hipStream_t s) {
     if (p.rows <= 0 || p.T <= 0) return;
-    if (p.T <= 64) {
+    if (p.T <= 64 && (p.kx == nullptr || p.Tk <= 64)) {
         dim3 grid((p.T + 31) / 32, p.H, p.rows);
         attn_short_kernel<1><<<grid, 64, 0, s>>>(p);
     } else {

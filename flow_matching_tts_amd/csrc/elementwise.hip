@@ -260,7 +260,7 @@ adaln_kernel(LnParams p, int tpw) {
         float sum = 0.0f;
 #pragma unroll
         for (int i = 0; i < V; ++i) sum += (cur[i][0] + cur[i][1]) + (cur[i][2] + cur[i][3]);
-        const float mean = wave_sum(sum) / (float)p.d;
+        const float mean = p.rms ? 0.0f : wave_sum(sum) / (float)p.d;
         float sq = 0.0f;
 #pragma unroll
         for (int i = 0; i < V; ++i) {
@@ -429,6 +429,49 @@ __global__ void assemble_cvec_kernel(const float* ct, const float* bs, const flo
     else cvec[o] = v;
 }
 
+__global__ void rope_table_kernel(float* tab, int T, int half, double base) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= T * half) return;
+    const int t = i / half, k = i - t * half;
+    const double a = (double)t * pow(base, -2.0 * k / (2.0 * half));
+    tab[2 * i] = (float)cos(a);
+    tab[2 * i + 1] = (float)sin(a);
+}
+
+// one thread per (token, pair of q|k columns)
+__global__ void rope_f32_kernel(float* qkv, long long n_tok, int ld, int T, int d, int hd, const float* tab,
+                                const int32_t* n_dev) {
+    const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    const long long n = n_dev ? min(n_tok, (long long)*n_dev) : n_tok;
+    if (i >= n * d) return;
+    const long long m = i / d;
+    const int pr = (int)(i - m * d);              // pair index over the 2d q|k columns
+    const int col = 2 * pr, k = (col % hd) >> 1;
+    const int t = (int)(m % T);
+    const float c = tab[2 * (t * (hd >> 1) + k)], sn = tab[2 * (t * (hd >> 1) + k) + 1];
+    float* x = qkv + m * ld + col;
+    const float a = x[0], b = x[1];
+    x[0] = a * c - b * sn;
+    x[1] = a * sn + b * c;
+}
+
+__global__ void swiglu_f32_kernel(const float* gu, float* act, long long M, int f, const int32_t* n_dev) {
+    const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    const long long Mv = n_dev ? min(M, (long long)*n_dev) : M;
+    if (i >= Mv * f) return;
+    const long long m = i / f;
+    const int j = (int)(i - m * f), b = j >> 4, e = j & 15;
+    const float* r = gu + m * 2 * f + 32 * b + e;
+    act[i] = silu(r[0]) * r[16];
+}
+
+__global__ void expand_context_kernel(const float* cond, float* xctx, int R, int cond0, long long per_row) {
+    const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    const int row = blockIdx.y, b = row / R, r = row - b * R;
+    if (i >= per_row) return;
+    xctx[(long long)row * per_row + i] = b >= cond0 ? cond[(long long)r * per_row + i] : 0.0f;
+}
+
 __global__ void prefix_init_kernel(const float* cproj, const float* bias, int R, int cond_branch0,
                                    int P, int T, int d, float* h) {
     const int n = blockIdx.x * blockDim.x + threadIdx.x;
@@ -528,6 +571,32 @@ void launch_assemble_cvec(const float* ct, const float* bs, const float* spkproj
                           int d, float* cvec, hipStream_t s, bf16* silu_bf16) {
     if (S <= 0) return;
     assemble_cvec_kernel<<<dim3((d + 255) / 256, nc, S), 256, 0, s>>>(ct, bs, spkproj, nc, d, cvec, silu_bf16);
+}
+
+void launch_rope_table(float* tab, int T, int hd, double base, hipStream_t s) {
+    const int n = T * (hd / 2);
+    if (n <= 0) return;
+    rope_table_kernel<<<(n + 255) / 256, 256, 0, s>>>(tab, T, hd / 2, base);
+}
+
+void launch_rope_f32(float* qkv, long long n_tok, int ld, int T, int d, int hd, const float* tab,
+                     const int32_t* n_dev, hipStream_t s) {
+    const long long n = n_tok * d;
+    if (n <= 0) return;
+    rope_f32_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(qkv, n_tok, ld, T, d, hd, tab, n_dev);
+}
+
+void launch_swiglu_f32(const float* gu, float* act, long long M, int f, const int32_t* n_dev, hipStream_t s) {
+    const long long n = M * f;
+    if (n <= 0) return;
+    swiglu_f32_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(gu, act, M, f, n_dev);
+}
+
+void launch_expand_context(const float* cond, float* xctx, int R, int nb, int cond0, long long per_row,
+                           hipStream_t s) {
+    if (R <= 0 || per_row <= 0) return;
+    expand_context_kernel<<<dim3((unsigned)((per_row + 255) / 256), nb * R), 256, 0, s>>>(cond, xctx, R, cond0,
+                                                                                        per_row);
 }
 
 void launch_prefix_init(const float* cproj, const float* bias, int R, int nb, int cond_branch0,

@@ -74,6 +74,20 @@ __device__ __forceinline__ void epi_store_vec4(const EpiParams& p, int m, int n,
         if constexpr (EPI == EPI_GELU_ACT) {
             v[0] = gelu_bf16(v[0]); v[1] = gelu_bf16(v[1]); v[2] = gelu_bf16(v[2]); v[3] = gelu_bf16(v[3]);
         }
+        if constexpr (EPI == EPI_QKV) {
+            if (p.rope != nullptr) {
+                // q or k columns n .. n+3 (n % 4 == 0): pairs (n, n+1) and (n+2, n+3) of their
+                // head turn by the table's angles of pair indices i0, i0 + 1 at position t
+                const int t = p.tok_row ? m - p.row_off[p.tok_row[m]] : m % p.T;
+                const int i0 = (n % p.rope_hd) >> 1;
+                const f32x4 cs = *(const f32x4*)(p.rope + ((long long)t * (p.rope_hd >> 1) + i0) * 2);
+                const float a0 = v[0], a1 = v[1], b0 = v[2], b1 = v[3];
+                v[0] = a0 * cs[0] - a1 * cs[1];
+                v[1] = a0 * cs[1] + a1 * cs[0];
+                v[2] = b0 * cs[2] - b1 * cs[3];
+                v[3] = b0 * cs[3] + b1 * cs[2];
+            }
+        }
         bf16x4 b;
         b[0] = (bf16)v[0]; b[1] = (bf16)v[1]; b[2] = (bf16)v[2]; b[3] = (bf16)v[3];
         *(bf16x4*)((bf16*)p.out + (long long)m * p.ldo + n) = b;
@@ -132,6 +146,29 @@ __device__ __forceinline__ void epi_block(const EpiParams& p, const f32x16& acc,
 #pragma unroll
         for (int r = 0; r < 4; ++r) wl[(8 * g + 4 * lh + r) * EPI_RP + li] = acc[g * 4 + r];
     __builtin_amdgcn_wave_barrier();
+    if constexpr (EPI == EPI_SWIGLU) {
+        // fused gate-up block: columns nb0 .. nb0 + 15 are the gate of features
+        // nb0 / 2 .. + 15, columns nb0 + 16 .. + 31 their up values. Lane: row
+        // (lane / 4) + 16 q, features 4 (lane % 4) .. + 3.
+        if (nb0 < N) {
+            const int c = (lane & 3) * 4;
+            const f32x4 bg = p.bias ? *(const f32x4*)(p.bias + nb0 + c) : f32x4{};
+            const f32x4 bu = p.bias ? *(const f32x4*)(p.bias + nb0 + 16 + c) : f32x4{};
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int row = (lane >> 2) + 16 * q, m = mb + row;
+                if (m >= M) continue;
+                const f32x4 g = *(const f32x4*)(wl + row * EPI_RP + c) + bg;
+                const f32x4 u = *(const f32x4*)(wl + row * EPI_RP + 16 + c) + bu;
+                bf16x4 o;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[e] = (bf16)(silu(g[e]) * u[e]);
+                *(bf16x4*)((bf16*)p.out + (long long)m * p.ldo + (nb0 >> 1) + c) = o;
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+        return;
+    }
     if constexpr (EPI == EPI_QKV) {
         if (nb0 >= p.d2) {
             // lane: column li, rows 16 lh .. 16 lh + 15 (consecutive sequence positions)

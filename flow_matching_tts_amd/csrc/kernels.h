@@ -15,6 +15,8 @@ enum Epi {
     EPI_INPROJ = 4,    // input projection of latent token m = r*Tx + t into every branch row
     EPI_VOUT = 5,      // velocity: out f32 [m, n] = frame valid ? acc + bias : 0
     EPI_QKV = 6,       // q|k columns -> out bf16 [m, 2d]; v columns -> vt bf16 [row, head, hd, Tp] (transposed)
+    EPI_SWIGLU = 7,    // fused gate-up: block of 32 columns 32b .. 32b+31 = 16 gate then 16 up columns of
+                       // features 16b .. 16b+15; out bf16 [m, 16b + i] = SiLU(gate_i + bias) * (up_i + bias)
 };
 
 struct EpiParams {
@@ -47,6 +49,10 @@ struct EpiParams {
     // a long K may then split K (the library picks the split; M * N * splits floats)
     float* split_ws = nullptr;
     long long split_ws_floats = 0;
+    // EPI_QKV, optional: rotary embedding of the q|k columns, table [T, rope_hd / 2] of
+    // (cos, sin) pairs by token position t (m - row_off[tok_row[m]], or m % T)
+    const float* rope = nullptr;
+    int rope_hd = 0;
 };
 
 // bf16 MFMA GEMM, A bf16 or f32 (rounded to bf16 while staging), W bf16 [N, K].
@@ -78,6 +84,13 @@ struct AttnParams {
     const int32_t* row_off = nullptr;
     // optional device flag: when it reads 0 every block exits at once (a skipped block)
     const int32_t* active = nullptr;
+    // cross-attention: keys come from kx instead of the row's own tokens, Tk per row
+    // (row i's keys at kx + i * Tk * ldkx; bf16 path: keys only, values in vt as
+    // usual; fp32 path: [key | value] rows of 2d); kv_len / kvalid / tile_full and
+    // Tp then describe those Tk keys. Null: self-attention.
+    const void* kx = nullptr;
+    long long ldkx = 0;
+    int Tk = 0;
 };
 void launch_attention_bf16(const AttnParams& p, hipStream_t s);
 // whether the bf16 attention's LDS (key ring plus per-key tables) holds sequences of T keys
@@ -94,6 +107,7 @@ struct LnParams {
     RowMod shift, scale;      // RowMod evaluated on the OUTPUT token index
     int out_bf16;
     const int32_t* n_dev = nullptr;   // optional device count of output tokens (at most n_out)
+    int rms = 0;                      // RMSNorm h / sqrt(mean(h^2) + 1e-6) instead of LayerNorm
 };
 void launch_adaln(const LnParams& p, hipStream_t s);
 
@@ -151,6 +165,17 @@ void launch_timestep_embedding(float* temb, int n_eval, int F, int kind, int S, 
 // index of the last valid frame (P if none); kvalid[r, t] = t < kv_len_out[r] and
 // (t < P or mask[r, t - P] != 0 or no mask), zero for t in [T, Tp); tile_full[r, i]
 // = 1 when keys 64i .. 64i+63 are all valid.
+// Rotary table tab[t, i] = (cos, sin)(t * base^(-2i / hd)), t < T, i < hd / 2 (angles in fp64).
+void launch_rope_table(float* tab, int T, int hd, double base, hipStream_t s);
+// In-place rotary embedding of the q and k columns (0 .. 2d) of fp32 rows qkv [n_tok, ld],
+// token m at position m % T; n_dev optional device token count.
+void launch_rope_f32(float* qkv, long long n_tok, int ld, int T, int d, int hd, const float* tab,
+                     const int32_t* n_dev, hipStream_t s);
+// act[m, 16b + i] = SiLU(gu[m, 32b + i]) * gu[m, 32b + 16 + i] (fp32, the interleaved gate-up rows).
+void launch_swiglu_f32(const float* gu, float* act, long long M, int f, const int32_t* n_dev, hipStream_t s);
+// Context of every branch row: xctx[b*R + r] = b >= cond0 ? cond[r] : 0 (per_row floats each).
+void launch_expand_context(const float* cond, float* xctx, int R, int nb, int cond0, long long per_row,
+                           hipStream_t s);
 void launch_key_prep(const uint8_t* mask, int mask_stride, const int32_t* kv_len_in, int R, int P,
                      int T, int Tp, int32_t* kv_len_out, uint8_t* kvalid, uint8_t* tile_full,
                      hipStream_t s);

@@ -46,6 +46,7 @@ cfm_status fail(cfm_status s, const char* fmt, ...) {
 }
 
 constexpr long long kMaxOperandBytes = (1LL << 31) - 256;
+constexpr int kSwigluGroup = 16;          // gate/up row interleave of the fused SwiGLU FC1 (half a 32-column block)
 constexpr size_t kSplitKTokens = 4096;   // batches up to this many tokens may split K
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -58,8 +59,14 @@ cfm_status check_config(const cfm_config* c) {
         c->t_freq_dim <= 0 || c->max_requests < 0 || c->max_frames < 0 || c->max_steps < 0)
         return fail(CFM_E_VALUE, "negative or zero size in config");
     if (c->dtype != CFM_F32 && c->dtype != CFM_BF16) return fail(CFM_E_UNSUPPORTED, "dtype %d", c->dtype);
-    if (c->cond_mode != CFM_COND_CHANNEL && c->cond_mode != CFM_COND_PREFIX)
+    if (c->cond_mode != CFM_COND_CHANNEL && c->cond_mode != CFM_COND_PREFIX && c->cond_mode != CFM_COND_CROSS)
         return fail(CFM_E_UNSUPPORTED, "cond_mode %d", c->cond_mode);
+    if (c->norm != CFM_NORM_LAYER && c->norm != CFM_NORM_RMS) return fail(CFM_E_UNSUPPORTED, "norm %d", c->norm);
+    if (c->mlp != CFM_MLP_GELU && c->mlp != CFM_MLP_SWIGLU) return fail(CFM_E_UNSUPPORTED, "mlp %d", c->mlp);
+    if (c->mlp == CFM_MLP_SWIGLU && c->ffn_dim % 16)
+        return fail(CFM_E_UNSUPPORTED, "the SwiGLU MLP needs ffn_dim %% 16 == 0");
+    if (c->rope && !(std::isfinite(c->rope_base) && c->rope_base > 0.0f))
+        return fail(CFM_E_VALUE, "rope_base must be positive and finite");
     if (c->n_branches < 1 || c->n_branches > 3) return fail(CFM_E_UNSUPPORTED, "n_branches %d", c->n_branches);
     if (c->d_model % c->n_heads) return fail(CFM_E_UNSUPPORTED, "d_model %% n_heads != 0");
     const int hd = c->d_model / c->n_heads;
@@ -75,9 +82,11 @@ cfm_status check_config(const cfm_config* c) {
         const long long es = c->dtype == CFM_BF16 ? 2 : 4;
         const long long P = c->cond_mode == CFM_COND_PREFIX ? c->n_prefix : 0;
         const long long tokens = (long long)c->n_branches * c->max_requests * round8(c->max_frames + P);
-        const long long wide = std::max<long long>(3LL * c->d_model, c->ffn_dim);
-        const long long cond_rows = (long long)c->max_requests * (P > 0 ? P : c->max_frames);
-        if (tokens * wide * es >= kMaxOperandBytes ||
+        const long long wide = std::max<long long>(3LL * c->d_model, 2LL * c->ffn_dim);
+        const long long cond_rows = (long long)c->max_requests * (c->cond_mode == CFM_COND_CHANNEL ? c->max_frames : c->n_prefix);
+        const long long ctx_rows = c->cond_mode == CFM_COND_CROSS ? (long long)c->n_branches * c->max_requests * c->n_prefix : 0;
+        if (tokens * wide * es >= kMaxOperandBytes || ctx_rows * 2LL * c->d_model * es >= kMaxOperandBytes ||
+            ctx_rows * c->cond_dim * 4 >= kMaxOperandBytes ||
             (long long)c->max_requests * c->max_frames * c->latent_dim * 4 >= kMaxOperandBytes ||
             cond_rows * std::max(c->cond_dim, c->latent_dim) * 4 >= kMaxOperandBytes)
             return fail(CFM_E_UNSUPPORTED, "capacity too large: an activation operand would exceed 2 GiB");
@@ -97,10 +106,15 @@ cfm_status check_config(const cfm_config* c) {
         if (c->dtype == CFM_BF16 && !attention_bf16_fits(c->max_frames + P))
             return fail(CFM_E_UNSUPPORTED, "max_frames + n_prefix = %lld: the attention key tables exceed LDS",
                         (long long)c->max_frames + P);
+        if (c->dtype == CFM_BF16 && c->cond_mode == CFM_COND_CROSS && !attention_bf16_fits(c->n_prefix))
+            return fail(CFM_E_UNSUPPORTED, "n_prefix = %d context keys exceed the attention's LDS tables", c->n_prefix);
     }
     if (c->cond_mode == CFM_COND_PREFIX) {
         if (c->n_prefix <= 0) return fail(CFM_E_UNSUPPORTED, "prefix mode needs n_prefix > 0");
         if (c->cond_dim != c->latent_dim) return fail(CFM_E_UNSUPPORTED, "prefix mode needs cond_dim == latent_dim");
+    } else if (c->cond_mode == CFM_COND_CROSS) {
+        if (c->n_prefix <= 0) return fail(CFM_E_UNSUPPORTED, "cross mode needs n_prefix (context tokens) > 0");
+        if (c->cond_dim <= 0) return fail(CFM_E_UNSUPPORTED, "cross mode needs cond_dim > 0");
     } else {
         if (c->n_prefix != 0) return fail(CFM_E_UNSUPPORTED, "channel mode needs n_prefix == 0");
         if (c->cond_dim <= 0) return fail(CFM_E_UNSUPPORTED, "channel mode needs cond_dim > 0");
@@ -126,11 +140,12 @@ Manifest build_manifest(const cfm_config& c) {
     const size_t mat_es = c.dtype == CFM_BF16 ? 2 : 4;
     size_t off = 0;
     auto add = [&](const char* name, long long row0, long long col0, long long rows, long long cols,
-                   bool vec, bool packed) {
+                   bool vec, bool packed, int interleave = 0) {
         cfm_tensor_desc t;
         std::memset(&t, 0, sizeof t);
         std::snprintf(t.name, sizeof t.name, "%s", name);
         t.row0 = row0; t.col0 = col0; t.rows = rows; t.cols = cols;
+        t.interleave = interleave;
         t.dtype = vec ? CFM_F32 : mat_dt;
         t.ld = vec ? cols : round8(cols);
         const size_t es = vec ? 4 : mat_es;
@@ -163,15 +178,30 @@ Manifest build_manifest(const cfm_config& c) {
         add(nm, 0, 0, 1, 6 * d, true, l > 0);
     }
     add("final.ada.bias", 0, 0, 1, 2 * d, true, c.n_layers > 0);
+    // SwiGLU: the fused gate-up FC1 (2f rows, gate rows first) is stored interleaved
+    // in groups of 16, so every 32-column output block pairs 16 gate and 16 up columns
+    const bool swiglu = c.mlp == CFM_MLP_SWIGLU;
     for (int l = 0; l < c.n_layers; ++l) {
         const char* parts[4] = {"qkv", "proj", "fc1", "fc2"};
-        const long long rows[4] = {3 * d, d, f, d};
+        const long long rows[4] = {3 * d, d, swiglu ? 2 * f : f, d};
         const long long cols[4] = {d, d, d, f};
         for (int i = 0; i < 4; ++i) {
+            const int il = swiglu && i == 2 ? kSwigluGroup : 0;
             std::snprintf(nm, sizeof nm, "blocks.%d.%s.weight", l, parts[i]);
-            add(nm, 0, 0, rows[i], cols[i], false, false);
+            add(nm, 0, 0, rows[i], cols[i], false, false, il);
             std::snprintf(nm, sizeof nm, "blocks.%d.%s.bias", l, parts[i]);
-            add(nm, 0, 0, 1, rows[i], true, false);
+            add(nm, 0, 0, 1, rows[i], true, false, il);
+        }
+        if (c.cond_mode == CFM_COND_CROSS) {
+            const char* xp[3] = {"q", "kv", "out"};
+            const long long xr[3] = {d, 2 * d, d};
+            const long long xc[3] = {d, c.cond_dim, d};
+            for (int i = 0; i < 3; ++i) {
+                std::snprintf(nm, sizeof nm, "blocks.%d.xattn.%s.weight", l, xp[i]);
+                add(nm, 0, 0, xr[i], xc[i], false, false);
+                std::snprintf(nm, sizeof nm, "blocks.%d.xattn.%s.bias", l, xp[i]);
+                add(nm, 0, 0, 1, xr[i], true, false);
+            }
         }
     }
     add("final.out.weight", 0, 0, C, d, false, false);
@@ -188,7 +218,8 @@ Slot find(const Manifest& m, const char* name, long long col0 = 0) {
 
 struct Layout {   // workspace regions, byte offsets
     size_t h, act, big, vt, v, cproj, temb, tpre, ct, spkproj, cvec, mod, kvlen, kvalid, tfull, rowoff, tokrow,
-        xmid, lanes, probe, resid, cstate, cparts, splitk, total;
+        xmid, lanes, probe, resid, cstate, cparts, splitk, rope, gu, unit, xctx, xk, xvt, xkvlen, xkvalid, xtfull,
+        total;
 };
 
 inline long long round64(long long v) { return (v + 63) / 64 * 64; }
@@ -200,12 +231,14 @@ Layout plan_workspace(const cfm_config& c) {
     const size_t N = (size_t)c.n_branches * Rm, d = c.d_model;
     // packed layout of masked batches (bf16 path, frame-aligned condition): rows
     // are rounded up to 8 tokens, so token buffers hold N * round8(T) tokens
-    const bool packable = c.dtype == CFM_BF16 && c.cond_mode == CFM_COND_CHANNEL;
+    const bool packable = c.dtype == CFM_BF16 && c.cond_mode != CFM_COND_PREFIX;
     const size_t T = Tx + P, TT = packable ? (T + 7) / 8 * 8 : T;
-    const size_t Tc = c.cond_mode == CFM_COND_PREFIX ? P : Tx;
+    const size_t Tc = c.cond_mode == CFM_COND_PREFIX ? P : c.cond_mode == CFM_COND_CHANNEL ? Tx : 0;
     const size_t nc = 1 + (c.spk_dim > 0 ? Rm : 0);
     const size_t ML = (6 * (size_t)c.n_layers + 2) * d;
     const size_t wide = std::max<size_t>(3 * d, c.ffn_dim);
+    const bool cross = c.cond_mode == CFM_COND_CROSS;
+    const size_t Tk = cross ? c.n_prefix : 0, Tkp = (size_t)round64(Tk), L_ = c.n_layers;
     Layout L;
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, 256); return o; };
@@ -236,6 +269,21 @@ Layout plan_workspace(const cfm_config& c) {
     // split-K partial products of the gated-residual GEMMs (N = d) of small batches:
     // up to 4 fp32 planes of [tokens, d]; large batches never split
     L.splitk = take(c.dtype == CFM_BF16 && N * TT <= kSplitKTokens ? 4 * N * TT * d * 4 : 0);
+    // rotary table: (cos, sin) of every token position and pair index (positions up to
+    // the row capacity rounded to 8: the packed layout's alignment tokens have some)
+    L.rope = take(c.rope ? round8(T) * (d / c.n_heads / 2) * 2 * 4 : 0);
+    // fp32 SwiGLU: the GEMM's interleaved gate-up output before the SwiGLU kernel
+    L.gu = take(c.dtype == CFM_F32 && c.mlp == CFM_MLP_SWIGLU ? N * TT * 2 * c.ffn_dim * 4 : 0);
+    L.unit = take(2 * d * 4);                            // d zeros then d ones (unmodulated norm, ungated residual)
+    // cross-attention: the context of every branch row, then per layer its keys and
+    // values (bf16: K [rows, Tk, d] and V^T [rows, H, 64, Tk rounded to 64]; fp32:
+    // [rows, Tk, 2d] key | value rows), and the key tables of the Tk context keys
+    L.xctx = take(cross ? N * Tk * c.cond_dim * 4 : 0);
+    L.xk = take(cross ? L_ * N * Tk * d * (c.dtype == CFM_BF16 ? 2 : 8) : 0);
+    L.xvt = take(cross && c.dtype == CFM_BF16 ? L_ * N * d * Tkp * 2 : 0);
+    L.xkvlen = take(cross ? Rm * 4 : 0);
+    L.xkvalid = take(cross ? Rm * Tkp : 0);
+    L.xtfull = take(cross ? Rm * Tkp / 64 : 0);
     L.total = off;
     return L;
 }
@@ -250,7 +298,7 @@ struct cfm_ctx {
     Manifest man;
     Layout lay;
     Slot t1w, t1b, t2w, t2b, spkw, spkb, inxw, incw, inb, adaw, adab, outw, outb;
-    struct LayerW { Slot qkvw, qkvb, projw, projb, fc1w, fc1b, fc2w, fc2b; };
+    struct LayerW { Slot qkvw, qkvb, projw, projb, fc1w, fc1b, fc2w, fc2b, xqw, xqb, xkvw, xkvb, xow, xob; };
     std::vector<LayerW> layers;
     // kernel timing
     int prof_class = -1, prof_cap = 0, prof_used = 0, prof_dropped = 0;
@@ -366,6 +414,11 @@ cfm_status cfm_create(const cfm_config* cfg, const void* weights, void* workspac
         L.projw = s("proj", "weight"); L.projb = s("proj", "bias");
         L.fc1w = s("fc1", "weight"); L.fc1b = s("fc1", "bias");
         L.fc2w = s("fc2", "weight"); L.fc2b = s("fc2", "bias");
+        if (cfg->cond_mode == CFM_COND_CROSS) {
+            L.xqw = s("xattn.q", "weight"); L.xqb = s("xattn.q", "bias");
+            L.xkvw = s("xattn.kv", "weight"); L.xkvb = s("xattn.kv", "bias");
+            L.xow = s("xattn.out", "weight"); L.xob = s("xattn.out", "bias");
+        }
         c->layers.push_back(L);
     }
     *out_ctx = c;
@@ -548,7 +601,10 @@ cfm_status cfm_sample_ex(cfm_ctx* c, const float* x0, const float* cond, const f
 
     const bool bf = g.dtype == CFM_BF16;
     const bool prefix = g.cond_mode == CFM_COND_PREFIX;
+    const bool cross = g.cond_mode == CFM_COND_CROSS;
+    const bool rms = g.norm == CFM_NORM_RMS, swiglu = g.mlp == CFM_MLP_SWIGLU;
     const int P = prefix ? g.n_prefix : 0;
+    const int Tk = cross ? g.n_prefix : 0, Tkp = (int)round64(Tk);
     const int T = Tx + P, N = nb * R;
     const int nc = 1 + (g.spk_dim > 0 ? R : 0);
     const long long ML = (6LL * L + 2) * d;
@@ -579,6 +635,16 @@ cfm_status cfm_sample_ex(cfm_ctx* c, const float* x0, const float* cond, const f
     // block-residual cache: front blocks [0, cf), middle [cf, cb), back [cb, L)
     const int cf = std::min(op.c_front, L), cb = std::max(cf, L - op.c_back);
     const bool caching = op.cache && cf < cb;
+    float* rope_tab = g.rope ? wsp<float>(c, ly.rope) : nullptr;
+    float* gu = wsp<float>(c, ly.gu);
+    float* unit = wsp<float>(c, ly.unit);               // d zeros, then d ones
+    float* xctx = wsp<float>(c, ly.xctx);
+    int32_t* xkvlen = wsp<int32_t>(c, ly.xkvlen);
+    uint8_t* xkvalid = wsp<uint8_t>(c, ly.xkvalid);
+    uint8_t* xtfull = wsp<uint8_t>(c, ly.xtfull);
+    // per layer: keys (bf16 [N*Tk, d]; fp32 key|value rows [N*Tk, 2d]) and bf16 V^T
+    auto xk_of = [&](int l) { return c->ws + ly.xk + (size_t)l * N * Tk * d * (bf ? 2 : 8); };
+    auto xvt_of = [&](int l) { return (bf16*)(c->ws + ly.xvt) + (size_t)l * N * d * Tkp; };
     int32_t* kvlen = wsp<int32_t>(c, ly.kvlen);
     uint8_t* kvalid = wsp<uint8_t>(c, ly.kvalid);
     uint8_t* tfull = wsp<uint8_t>(c, ly.tfull);
@@ -590,7 +656,7 @@ cfm_status cfm_sample_ex(cfm_ctx* c, const float* x0, const float* cond, const f
     // nothing). The outputs are those of the padded layout: every operation but
     // attention is token-local, attention masks every key from kv_len on, and the
     // frames cut off are masked keys whose velocities are never used.
-    const bool packable = bf && !prefix;
+    const bool packable = bf && !prefix;   // channel or cross condition: frame-aligned rows
     const bool packed = packable && (frame_mask != nullptr || adaptive);
     const long long Trow = packed ? (T + 7) / 8 * 8 : T;     // token capacity per row
     int32_t* rowoff = packed ? wsp<int32_t>(c, ly.rowoff) : nullptr;
@@ -654,7 +720,33 @@ cfm_status cfm_sample_ex(cfm_ctx* c, const float* x0, const float* cond, const f
         ep.out = cproj;
         ep.ldo = d;
         if (prefix) gemm(CFM_K_HOISTED, true, cond, C, c->inxw, R * P, d, C, EPI_F32, ep);
-        else gemm(CFM_K_HOISTED, true, cond, g.cond_dim, c->incw, R * Tx, d, g.cond_dim, EPI_F32, ep);
+        else if (!cross) gemm(CFM_K_HOISTED, true, cond, g.cond_dim, c->incw, R * Tx, d, g.cond_dim, EPI_F32, ep);
+    }
+    // block variants: the rotary table, the unit vectors, and the cross-attention keys
+    // and values of every layer (the context is fixed over the steps)
+    timed(c, CFM_K_HOISTED, s, [&] {
+        if (rope_tab) launch_rope_table(rope_tab, (int)round8(T), hd, (double)g.rope_base, s);
+        launch_fill_i32((int32_t*)unit, d, 0, s);
+        launch_fill_i32((int32_t*)unit + d, d, 0x3f800000, s);   // 1.0f
+    });
+    if (cross) {
+        timed(c, CFM_K_HOISTED, s, [&] {
+            launch_key_prep(nullptr, Tk, nullptr, R, 0, Tk, Tkp, xkvlen, xkvalid, xtfull, s);
+            launch_expand_context(cond, xctx, R, nb, nb == 1 ? 0 : 1, (long long)Tk * g.cond_dim, s);
+        });
+        for (int l = 0; l < L; ++l) {
+            const auto& W = c->layers[l];
+            EpiParams ek;
+            ek.bias = wp<float>(c, W.xkvb);
+            ek.out = xk_of(l);
+            if (bf) {   // keys to [row token, d], values transposed per head
+                ek.ldo = d; ek.vt = xvt_of(l); ek.H = H; ek.T = Tk; ek.Tp = Tkp; ek.d2 = d;
+                gemm(CFM_K_HOISTED, true, xctx, g.cond_dim, W.xkvw, N * Tk, 2 * d, g.cond_dim, EPI_QKV, ek);
+            } else {
+                ek.ldo = 2 * d;
+                gemm(CFM_K_HOISTED, true, xctx, g.cond_dim, W.xkvw, N * Tk, 2 * d, g.cond_dim, EPI_ACT, ek);
+            }
+        }
     }
 
     // One estimator evaluation at evaluation index j over nbe branch rows per
@@ -693,7 +785,7 @@ cfm_status cfm_sample_ex(cfm_ctx* c, const float* x0, const float* cond, const f
             ep.bias = wp<float>(c, c->inb);
             ep.out = h; ep.ldo = d;
             ep.R = R; ep.Tx = Tx; ep.T = T; ep.P = P; ep.nb = nbe; ep.cond_branch0 = cond0;
-            ep.cproj = prefix ? nullptr : cproj;
+            ep.cproj = prefix || cross ? nullptr : cproj;
             ep.row_off = rowoff;
             gemm(CFM_K_GEMM_IN, true, xl, C, c->inxw, R * Tx, d, C, EPI_INPROJ, ep);
         }
@@ -719,17 +811,20 @@ cfm_status cfm_sample_ex(cfm_ctx* c, const float* x0, const float* cond, const f
             LnParams ln;
             ln.h = h; ln.y = act; ln.d = d; ln.n_out = NTk; ln.Tin = T; ln.Tout = T; ln.off = 0;
             ln.shift = rowmod(ml + 0 * d, T); ln.scale = rowmod(ml + 1 * d, T); ln.out_bf16 = bf;
-            ln.n_dev = ntok_l;
+            ln.n_dev = ntok_l; ln.rms = rms;
             timed(c, CFM_K_ADALN, s, [&] { launch_adaln(ln, s); });
             EpiParams e1; e1.bias = wp<float>(c, W.qkvb); e1.out = big;
-            if (bf) {   // q|k rows of 2d, v transposed per head for the attention tiles
+            if (bf) {   // q|k rows of 2d (rotated in the epilogue), v transposed per head
                 e1.ldo = 2 * d; e1.vt = vt; e1.H = H; e1.T = T; e1.Tp = Tp; e1.d2 = 2 * d;
                 e1.tok_row = tokrow; e1.row_off = rowoff; e1.m_dev = ntok_l;
+                e1.rope = rope_tab; e1.rope_hd = hd;
             } else {
                 e1.ldo = 3 * d;
                 e1.m_dev = ntok_l;
             }
             gemm(CFM_K_GEMM_QKV, false, act, d, W.qkvw, (int)NTk, 3 * d, d, bf ? EPI_QKV : EPI_ACT, e1);
+            if (rope_tab && !bf)
+                timed(c, CFM_K_GEMM_QKV, s, [&] { launch_rope_f32((float*)big, NTk, 3 * d, T, d, hd, rope_tab, ntok_l, s); });
             ap.active = mid ? cstate + 4 : nullptr;
             timed(c, CFM_K_ATTENTION, s, [&] {
                 if (bf) launch_attention_bf16(ap, s); else launch_attention_f32(ap, s);
@@ -738,10 +833,44 @@ cfm_status cfm_sample_ex(cfm_ctx* c, const float* x0, const float* cond, const f
             e2.m_dev = ntok_l;
             e2.split_ws = splitk; e2.split_ws_floats = splitk_floats;
             gemm(CFM_K_GEMM_PROJ, false, act, d, W.projw, (int)NTk, d, d, EPI_GATED, e2);
+            if (cross) {
+                // cross-attention sublayer: unmodulated norm, queries, attention over the
+                // row's context keys, ungated residual (gate vector of ones)
+                LnParams lx = ln;
+                RowMod zero = rowmod(unit, T), one = rowmod(unit + d, T);
+                zero.spk_branch = one.spk_branch = -1;
+                lx.shift = zero; lx.scale = zero;
+                timed(c, CFM_K_ADALN, s, [&] { launch_adaln(lx, s); });
+                EpiParams eq; eq.bias = wp<float>(c, W.xqb); eq.out = big; eq.ldo = bf ? 2 * d : 3 * d;
+                eq.m_dev = ntok_l;
+                gemm(CFM_K_GEMM_XATTN, false, act, d, W.xqw, (int)NTk, d, d, EPI_ACT, eq);
+                AttnParams ax = ap;
+                const int kv0 = nbe == 1 ? (nb - 1) * R : 0;      // rows of the fully conditioned branch
+                ax.kx = xk_of(l) + (size_t)kv0 * Tk * d * (bf ? 2 : 8);
+                ax.ldkx = bf ? d : 2 * d; ax.Tk = Tk;
+                ax.vt = xvt_of(l) + (size_t)kv0 * d * Tkp; ax.Tp = Tkp;
+                ax.kv_len = xkvlen; ax.kv_mod = R; ax.key_mask = nullptr; ax.mask_stride = 0; ax.P = 0;
+                ax.kvalid = xkvalid; ax.tile_full = xtfull;
+                timed(c, CFM_K_XATTN, s, [&] {
+                    if (bf) launch_attention_bf16(ax, s); else launch_attention_f32(ax, s);
+                });
+                EpiParams eo; eo.bias = wp<float>(c, W.xob); eo.out = h; eo.ldo = d; eo.gate = one;
+                eo.m_dev = ntok_l;
+                eo.split_ws = splitk; eo.split_ws_floats = splitk_floats;
+                gemm(CFM_K_GEMM_XATTN, false, act, d, W.xow, (int)NTk, d, d, EPI_GATED, eo);
+            }
             ln.shift = rowmod(ml + 3 * d, T); ln.scale = rowmod(ml + 4 * d, T);
             timed(c, CFM_K_ADALN, s, [&] { launch_adaln(ln, s); });
             EpiParams e3; e3.bias = wp<float>(c, W.fc1b); e3.out = big; e3.ldo = f; e3.m_dev = ntok_l;
-            gemm(CFM_K_GEMM_FC1, false, act, d, W.fc1w, (int)NTk, f, d, EPI_GELU_ACT, e3);
+            if (!swiglu) {
+                gemm(CFM_K_GEMM_FC1, false, act, d, W.fc1w, (int)NTk, f, d, EPI_GELU_ACT, e3);
+            } else if (bf) {   // fused gate-up GEMM, SwiGLU in its epilogue
+                gemm(CFM_K_GEMM_FC1, false, act, d, W.fc1w, (int)NTk, 2 * f, d, EPI_SWIGLU, e3);
+            } else {
+                e3.out = gu; e3.ldo = 2 * f;
+                gemm(CFM_K_GEMM_FC1, false, act, d, W.fc1w, (int)NTk, 2 * f, d, EPI_ACT, e3);
+                timed(c, CFM_K_GEMM_FC1, s, [&] { launch_swiglu_f32(gu, (float*)big, NTk, f, ntok_l, s); });
+            }
             EpiParams e4; e4.bias = wp<float>(c, W.fc2b); e4.out = h; e4.ldo = d; e4.gate = rowmod(ml + 5 * d, T);
             e4.m_dev = ntok_l;
             e4.split_ws = splitk; e4.split_ws_floats = splitk_floats;
@@ -753,7 +882,7 @@ cfm_status cfm_sample_ex(cfm_ctx* c, const float* x0, const float* cond, const f
             const float* mf = modk + (long long)L * 6 * d;
             LnParams ln;
             ln.h = h; ln.y = act; ln.d = d; ln.n_out = (long long)Ne * Tx; ln.Tin = T; ln.Tout = Tx; ln.off = P;
-            ln.shift = rowmod(mf, Tx); ln.scale = rowmod(mf + d, Tx); ln.out_bf16 = bf;
+            ln.shift = rowmod(mf, Tx); ln.scale = rowmod(mf + d, Tx); ln.out_bf16 = bf; ln.rms = rms;
             if (packed) { ln.n_out = NTk; ln.Tin = ln.Tout = 1; ln.n_dev = ntok; }   // tokens map one to one
             timed(c, CFM_K_ADALN, s, [&] { launch_adaln(ln, s); });
             EpiParams ep; ep.bias = wp<float>(c, c->outb); ep.out = vel; ep.ldo = C;
@@ -858,18 +987,20 @@ cfm_status cfm_gemm_bf16(const void* A, int a_is_f32, int lda, const void* W, in
     if (M < 0 || N < 0 || K < 0) return fail(CFM_E_VALUE, "negative size");
     if (!(tile == 0 || tile == 1 || tile == 6 || tile == 10 || tile == 14 || tile == 15) || (tile > 1 && a_is_f32))
         return fail(CFM_E_VALUE, "tile %d", tile);
-    if (epilogue < 0 || epilogue > 3) return fail(CFM_E_VALUE, "epilogue %d", epilogue);
+    if (epilogue < 0 || epilogue > 4) return fail(CFM_E_VALUE, "epilogue %d", epilogue);
+    if (epilogue == 4 && N % 32) return fail(CFM_E_SHAPE, "the SwiGLU epilogue needs N %% 32 == 0");
     if (M == 0 || N == 0) return CFM_OK;
     if (A == nullptr || W == nullptr || C == nullptr) return fail(CFM_E_NULL, "A, W or C is NULL");
     if (epilogue == 3 && gate == nullptr) return fail(CFM_E_NULL, "gate is NULL");
     const int kq = a_is_f32 ? 4 : 8;
-    if (K % kq || lda % kq || ldw % 8 || lda < K || ldw < round8(K) || ldc < N || (N > 3 && ldc % 4))
+    const int ncols = epilogue == 4 ? N / 2 : N;
+    if (K % kq || lda % kq || ldw % 8 || lda < K || ldw < round8(K) || ldc < ncols || (ncols > 3 && ldc % 4))
         return fail(CFM_E_SHAPE, "K/lda/ldw/ldc do not meet the layout rules");
     if (!aligned16(A) || !aligned16(W) || !aligned16(C) || (bias && !aligned16(bias)) || (gate && !aligned16(gate)))
         return fail(CFM_E_SHAPE, "A, W, C, bias and gate must be 16-byte aligned");
     if ((long long)M * lda * (a_is_f32 ? 4 : 2) >= kMaxOperandBytes || (long long)N * ldw * 2 >= kMaxOperandBytes)
         return fail(CFM_E_SHAPE, "operand above 2 GiB");
-    static const int map[4] = {EPI_F32, EPI_ACT, EPI_GELU_ACT, EPI_GATED};
+    static const int map[5] = {EPI_F32, EPI_ACT, EPI_GELU_ACT, EPI_GATED, EPI_SWIGLU};
     EpiParams ep;
     ep.bias = bias;
     ep.out = C;

@@ -65,20 +65,42 @@ typedef enum cfm_status {
 } cfm_status;
 
 typedef enum cfm_dtype { CFM_F32 = 0, CFM_BF16 = 1 } cfm_dtype;
-typedef enum cfm_cond_mode { CFM_COND_CHANNEL = 0, CFM_COND_PREFIX = 1 } cfm_cond_mode;
+typedef enum cfm_cond_mode { CFM_COND_CHANNEL = 0, CFM_COND_PREFIX = 1, CFM_COND_CROSS = 2 } cfm_cond_mode;
+/* Block variants (VoiceHub "Diffusion and flow TTS optimization", section "Custom
+ * Triton and CUDA kernels": RMSNorm and SwiGLU patterns; vLLM-Omni TTS blog, section
+ * "CFM/LocDiT decode-tail batching": the LocDiT's fused gate-up MLP). */
+typedef enum cfm_norm { CFM_NORM_LAYER = 0, CFM_NORM_RMS = 1 } cfm_norm;
+typedef enum cfm_mlp { CFM_MLP_GELU = 0, CFM_MLP_SWIGLU = 1 } cfm_mlp;
 
 /* Model and capacity description. Plain data; copied by cfm_create.
  *   cond_mode CHANNEL: cond is [R, Tx, cond_dim], concatenated after the latent
  *                      channels of each frame before the input projection.
  *   cond_mode PREFIX:  cond is [R, n_prefix, latent_dim]: condition frames placed
  *                      before the Tx latent frames (cond_dim must equal latent_dim).
+ *   cond_mode CROSS:   cond is a context [R, n_prefix, cond_dim] that every block
+ *                      reads through a cross-attention sublayer placed between its
+ *                      self-attention and its MLP, h += Wo attn(Wq N(h) + bq, K, V) + bo,
+ *                      N the block's norm without modulation, [K | V] = Wkv ctx + bkv
+ *                      over all n_prefix context tokens (computed once per call: the
+ *                      context is fixed over the steps; VoiceHub, "Recommended
+ *                      optimization boundaries" table, rows Echo and Irodori-TTS:
+ *                      cached condition keys/values). The input projection sees the
+ *                      latent alone; the unconditional branch sees a zero context.
+ *   norm:  LAYER (h - mean) / sqrt(var + 1e-6), or RMS h / sqrt(mean(h^2) + 1e-6);
+ *          every norm of the estimator follows it.
+ *   mlp:   GELU: FC2(GELU(FC1 u)); SWIGLU: FC1 is a fused gate-up weight of 2 ffn_dim
+ *          rows (gate rows first, as given), FC2(SiLU(gate) * up); needs ffn_dim % 16 == 0.
+ *   rope:  nonzero: rotary position embedding (RoFormer) of the self-attention
+ *          queries and keys: feature pairs (2i, 2i+1) of each head turn by the
+ *          angle p * rope_base^(-2i / head_dim), p the token's index in its row's
+ *          sequence (prefix tokens first); rope_base > 0 and finite.
  *   dtype BF16: weights and GEMM/attention operands bfloat16 with fp32
  *               accumulation; residual stream, LayerNorm statistics, softmax,
  *               modulation, velocities and x are fp32.
  *   dtype F32:  fp32 end to end.
  * Supported: d_model % 8 == 0, ffn_dim % 8 == 0, latent_dim % 4 == 0,
  * cond_dim % 4 == 0, t_freq_dim even and % 8 == 0, 1 <= n_branches <= 3;
- * BF16 needs head_dim == 64, F32 needs head_dim % 4 == 0 and head_dim <= 128. */
+ * BF16 needs head_dim == 64, F32 needs head_dim % 4 == 0 and head_dim <= 64. */
 typedef struct cfm_config {
     int32_t n_layers, d_model, n_heads, ffn_dim;
     int32_t latent_dim, cond_dim, cond_mode, n_prefix;
@@ -87,6 +109,10 @@ typedef struct cfm_config {
     int32_t n_branches;       /* CFG branch rows per request: 1, 2 or 3             */
     int32_t dtype;            /* cfm_dtype                                          */
     int32_t max_requests, max_frames, max_steps;   /* capacity of the workspace    */
+    int32_t norm;             /* cfm_norm                                           */
+    int32_t mlp;              /* cfm_mlp                                            */
+    int32_t rope;             /* 0 = off                                            */
+    float rope_base;          /* rotary frequency base (10000 in RoFormer)          */
 } cfm_config;
 
 /* One slot of the flat weight buffer. The slot holds
@@ -94,13 +120,19 @@ typedef struct cfm_config {
  * (PyTorch Linear convention: weight [out, in], bias [out]) with a row stride
  * of `ld` elements, starting `offset` bytes into the buffer. `dtype` is the
  * element type of the slot (matrices: the config dtype; biases: always F32).
+ * `interleave` = k > 0 reorders the slot's rows: the source rows form two halves
+ * (rows/2 each), and slot row group g (rows [2k g, 2k g + 2k)) holds rows
+ * [k g, k g + k) of the first half followed by rows [k g, k g + k) of the second
+ * half (for a bias, the same on its elements); 0 = source order. (The fused
+ * gate-up weight is stored this way, so that each 2k-wide output block of its
+ * GEMM holds k gate columns and the k up columns that pair with them.)
  * Bytes of the buffer not covered by a slot (row padding) must be zero. */
 typedef struct cfm_tensor_desc {
     char name[48];
     int64_t row0, col0, rows, cols, ld;
     int64_t offset;
     int32_t dtype;
-    int32_t reserved;
+    int32_t interleave;
 } cfm_tensor_desc;
 
 typedef struct cfm_ctx cfm_ctx;
@@ -130,7 +162,8 @@ cfm_status cfm_create(const cfm_config* cfg, const void* weights, void* workspac
 
 /* Runs the whole sampler: S = n_steps Euler steps over R = n_requests requests.
  *   x0         device fp32 [R, Tx, latent_dim]         noise (t = 0)
- *   cond       device fp32 [R, Tx, cond_dim] (CHANNEL) or [R, n_prefix, latent_dim] (PREFIX)
+ *   cond       device fp32 [R, Tx, cond_dim] (CHANNEL), [R, n_prefix, latent_dim] (PREFIX)
+ *              or [R, n_prefix, cond_dim] (CROSS)
  *   spk        device fp32 [R, spk_dim], or NULL when spk_dim == 0
  *   frame_mask device uint8 [R, Tx], 1 = valid frame, or NULL = all valid
  *   guidance   host fp32 [n_branches - 1] guidance scales (NULL allowed when n_branches == 1)
@@ -261,11 +294,14 @@ const char* cfm_last_error_detail(void);
  * SYNCHRONISES on those events (host wait) and returns the summed elapsed
  * milliseconds and the launch count since the last enable; the event pool holds
  * `capacity` launches (extra launches are not timed and counted in *dropped).
- * Class ids are the CFM_K_* values below. */
+ * Class ids are the CFM_K_* values below (XATTN: the cross-attention kernel of the
+ * CROSS mode; GEMM_XATTN: its query and output projections; a fp32 rotary or SwiGLU
+ * pass counts with its QKV or FC1 GEMM; the unmodulated cross-attention norm with
+ * ADALN). */
 enum {
     CFM_K_GEMM_QKV = 0, CFM_K_GEMM_PROJ = 1, CFM_K_GEMM_FC1 = 2, CFM_K_GEMM_FC2 = 3,
     CFM_K_ATTENTION = 4, CFM_K_ADALN = 5, CFM_K_CFG_EULER = 6, CFM_K_GEMM_IN = 7,
-    CFM_K_GEMM_OUT = 8, CFM_K_HOISTED = 9, CFM_K_COUNT = 10
+    CFM_K_GEMM_OUT = 8, CFM_K_HOISTED = 9, CFM_K_XATTN = 10, CFM_K_GEMM_XATTN = 11, CFM_K_COUNT = 12
 };
 cfm_status cfm_profile_enable(cfm_ctx* ctx, int kernel_class, int capacity);
 cfm_status cfm_profile_read(cfm_ctx* ctx, double* total_ms, int* launches, int* dropped);
@@ -290,7 +326,12 @@ cfm_status cfm_cfg_euler(const float* v, const float* w, int nb, float dt, const
  *   A device bf16 (a_is_f32 = 0) or fp32 (a_is_f32 = 1, rounded to bf16 on load)
  *   [M, K] row stride lda; W device bf16 [N, K] row stride ldw; bias device fp32
  *   [N] or NULL. epilogue 0: C fp32; 1: C bf16; 2: C bf16 of GELU(exact erf);
- *   3: gated residual C(fp32) += gate[n] * (acc + bias[n]) with gate device fp32 [N].
+ *   3: gated residual C(fp32) += gate[n] * (acc + bias[n]) with gate device fp32 [N];
+ *   4: SwiGLU of a fused gate-up weight stored interleaved in groups of 16 rows
+ *      (cfm_tensor_desc, interleave 16): C bf16 [M, N/2],
+ *      C[m, 16b + i] = SiLU(acc[m, 32b + i] + bias) * (acc[m, 32b + 16 + i] + bias),
+ *      N % 32 == 0 (vox-serve/VoiceHub "Custom Triton and CUDA kernels": SwiGLU;
+ *      vLLM-Omni "CFM/LocDiT decode-tail batching": fused gate-up MLP).
  * K % 8 == 0 (bf16 A) or K % 4 == 0 (fp32 A); lda, ldw multiples of 8 (bf16)
  * or 4 (fp32 A); ldw >= K rounded up to 8 with zero padding.
  * tile: 0 = chosen from the problem size (what cfm_sample uses); 1 = 128x128
@@ -300,7 +341,7 @@ cfm_status cfm_cfg_euler(const float* v, const float* w, int nb, float dt, const
  * CFM_E_VALUE, as does a tile other than 0 or 1 with an fp32 A operand. The GELU
  * of epilogue 2 is evaluated with an erfc approximation of relative error below
  * 1e-5 (bf16 rounding: 2^-9).
- * Layout rules (CFM_E_SHAPE otherwise): ldc >= N, and ldc % 4 == 0 when N > 3
+ * Layout rules (CFM_E_SHAPE otherwise): ldc >= N (N/2 for epilogue 4), and ldc % 4 == 0 when N > 3
  * (rows of four or more columns are written with vector stores); A, W, C, bias
  * and gate 16-byte aligned. */
 cfm_status cfm_gemm_bf16(const void* A, int a_is_f32, int lda, const void* W, int ldw,

@@ -44,7 +44,10 @@ def test_status_strings(lib):
     assert lib.cfm_status_string(99) == b"unknown status"
 
 
-@pytest.mark.parametrize("name", synth.WORKLOAD_ORDER)
+VARIANT_WORKLOADS = ["locdit_swiglu", "cross_dit", "tiny_f32_variants"]
+
+
+@pytest.mark.parametrize("name", synth.WORKLOAD_ORDER + VARIANT_WORKLOADS)
 def test_sizes_and_manifest_cover_every_parameter(lib, name):
     import flow_matching_tts_amd as F
     s = synth.workload(name)
@@ -73,16 +76,51 @@ def test_sizes_and_manifest_cover_every_parameter(lib, name):
     assert spans[-1][1] <= wb
 
 
-def test_pack_weights_places_every_value(lib):
+@pytest.mark.parametrize("name", ["tiny_f32", "tiny_f32_variants"])
+def test_pack_weights_places_every_value(lib, name):
     import flow_matching_tts_amd as F
-    s = synth.workload("tiny_f32")
+    s = synth.workload(name)
     cfg = config_for(s)
     W = synth.make_weights(s)
     buf = F.pack_weights(cfg, W)
+    n_il = 0
     for e in F.weight_manifest(cfg):
         src = W[e["name"]].reshape(-1, W[e["name"]].shape[-1]) if W[e["name"]].ndim == 2 else W[e["name"]][None]
         blk = buf[e["offset"]:e["offset"] + e["rows"] * e["ld"] * 4].view(np.float32).reshape(e["rows"], e["ld"])
-        np.testing.assert_array_equal(blk[:, :e["cols"]], src[e["row0"]:e["row0"] + e["rows"], e["col0"]:e["col0"] + e["cols"]])
+        want = src[e["row0"]:e["row0"] + e["rows"], e["col0"]:e["col0"] + e["cols"]]
+        if e["interleave"]:
+            # the fused gate-up FC1: groups of 16 gate rows alternate with the 16 up rows
+            # of the same features (elements for the bias)
+            n_il += 1
+            assert e["interleave"] == 16 and e["name"].startswith("blocks.") and ".fc1." in e["name"]
+            k, f = 16, (want.shape[0] if want.shape[0] > 1 else want.shape[1]) // 2
+            flat = want if want.shape[0] > 1 else want.T
+            perm = [(g // 2) * k + (g % 2) * f + i for g in range(2 * f // k) for i in range(k)]
+            want = flat[perm] if want.shape[0] > 1 else flat[perm].T
+        else:
+            assert not (e["name"].startswith("blocks.") and ".fc1." in e["name"] and s.mlp == "swiglu")
+        np.testing.assert_array_equal(blk[:, :e["cols"]], want)
+    assert n_il == (2 * s.n_layers if s.mlp == "swiglu" else 0)
+
+
+def test_variant_configs_are_validated(lib):
+    ctx = C.c_void_p()
+    fake = 1 << 20
+    base = synth.workload("tiny_f32_variants")
+    good = config_for(base)
+    ws = lib.cfm_workspace_bytes(C.byref(good))
+    assert ws > 0 and lib.cfm_create(C.byref(good), fake, fake, ws, C.byref(ctx)) == 0
+    lib.cfm_destroy(ctx)
+    for kw, code, text in ((dict(ffn_dim=104), 5, b"SwiGLU"), (dict(rope_base=0.0), 4, b"rope_base"),
+                           (dict(rope_base=float("inf")), 4, b"rope_base"), (dict(n_prefix=0), 5, b"cross")):
+        bad = config_for(base.replace(**kw))
+        assert lib.cfm_create(C.byref(bad), fake, fake, 1 << 40, C.byref(ctx)) == code, kw
+        assert text in lib.cfm_last_error_detail(), kw
+    for field, value in (("norm", 2), ("mlp", 2), ("cond_mode", 3)):
+        bad = config_for(base)
+        setattr(bad, field, value)
+        assert lib.cfm_create(C.byref(bad), fake, fake, 1 << 40, C.byref(ctx)) == 5, field
+    assert lib.cfm_weights_bytes(C.byref(config_for(base.replace(rope=False, rope_base=-1.0)))) > 0   # base unused
 
 
 def _cfg(**kw):
