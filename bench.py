@@ -36,7 +36,8 @@ import synth  # noqa: E402
 
 PEAK_BF16 = 2.5e15      # MI355X dense bf16 MFMA, FLOP/s
 PEAK_HBM = 8.0e12       # MI355X HBM3E, B/s
-MFMA_CLASSES = ["gemm_qkv", "gemm_proj", "gemm_fc1", "gemm_fc2", "attention", "gemm_in", "gemm_out"]
+MFMA_CLASSES = ["gemm_qkv", "gemm_proj", "gemm_fc1", "gemm_fc2", "attention", "gemm_in", "gemm_out",
+                "xattn", "gemm_xattn"]
 
 
 def log(*a):
@@ -52,18 +53,23 @@ def work_model(s, lengths):
     tok_v = nb * float(np.sum(Lv + P))                  # valid tokens over all rows
     x_v = float(np.sum(Lv))                              # valid latent frames over all requests
     attn = 4.0 * s.head_dim * H * nb * float(np.sum((Lv + P) ** 2))
+    f1 = 2 * f if s.mlp == "swiglu" else f               # fused gate-up FC1 width
+    cross = s.cond_mode == "cross"
     w = {
         "gemm_qkv": (2.0 * tok_v * 3 * d * d, L * S),
         "gemm_proj": (2.0 * tok_v * d * d, L * S),
-        "gemm_fc1": (2.0 * tok_v * f * d, L * S),
+        "gemm_fc1": (2.0 * tok_v * f1 * d, L * S),
         "gemm_fc2": (2.0 * tok_v * d * f, L * S),
         "attention": (attn, L * S),
         "gemm_in": (2.0 * x_v * d * C, S),
         "gemm_out": (2.0 * nb * x_v * C * d, S),
         # bytes: LN reads h fp32, writes bf16 (valid tokens); CFG+Euler reads x, writes x, reads nb v
-        "adaln": (tok_v * d * (4 + 2), 2 * L * S + S),
+        "adaln": (tok_v * d * (4 + 2), (3 if cross else 2) * L * S + S),
         "cfg_euler": (x_v * C * 4 * (2 + nb), S),
     }
+    if cross:   # queries of every valid token against the row's n_prefix context keys
+        w["xattn"] = (4.0 * s.head_dim * H * nb * float(np.sum(Lv)) * s.n_prefix, L * S)
+        w["gemm_xattn"] = (2.0 * tok_v * d * d, 2 * L * S)       # query and output projections
     return w
 
 
@@ -121,10 +127,15 @@ def cpu_baseline(s, W, I, max_workers: int):
     workload's S) for as many requests as there are worker processes (one request per
     process, one BLAS thread each), scaled to estimator evals/s like the GPU figure."""
     from oracle import sampler as O
-    cores = max(1, min(O.host_cores(), max_workers, s.n_requests))
+    variant = (s.norm, s.mlp, s.rope, s.cond_mode == "cross") != ("layer", "gelu", False, False)
+    cores = 1 if variant else max(1, min(O.host_cores(), max_workers, s.n_requests))
     reqs = list(range(cores))
     t0 = time.perf_counter()
-    O.sample(W, s, I["x0"], I["cond"], I["spk"], I["mask"], 1, s.guidance, requests=reqs, workers=cores)
+    if variant:     # the block-variant oracle runs its requests in one process
+        from oracle import variants as V
+        V.sample(W, s, I["x0"], I["cond"], I["spk"], I["mask"], 1, s.guidance, requests=reqs)
+    else:
+        O.sample(W, s, I["x0"], I["cond"], I["spk"], I["mask"], 1, s.guidance, requests=reqs, workers=cores)
     t = time.perf_counter() - t0
     evals = len(reqs) * s.n_branches * 1
     model, blas = host_description()
@@ -186,7 +197,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="mel_dit", choices=synth.WORKLOAD_ORDER)
+    ap.add_argument("--workload", default="mel_dit", choices=list(synth.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-workers", type=int, default=16)
     ap.add_argument("--no-kernel-timing", action="store_true")
@@ -319,8 +330,8 @@ def main():
                     "traffic": measured_traffic(dom, s.name),
                     "mean_launch_us": mean_s * 1e6, "launches": n,
                     "work_per_launch": work}
-        mf = sum(model[c][0] * model[c][1] for c in MFMA_CLASSES)
-        mt = sum(kernels[c]["ms_per_sample"] for c in MFMA_CLASSES) / 1e3
+        mf = sum(model[c][0] * model[c][1] for c in MFMA_CLASSES if c in model)
+        mt = sum(kernels[c]["ms_per_sample"] for c in MFMA_CLASSES if c in kernels) / 1e3
         gemm_attn_frac = mf / mt / PEAK_BF16
         for c, k in kernels.items():
             work_c, launches_c = model.get(c, (None, None))
@@ -332,7 +343,7 @@ def main():
             k["frac"] = rate / (PEAK_BF16 if c in MFMA_CLASSES else PEAK_HBM)
     else:
         roofline, gemm_attn_frac = None, None
-        mf = sum(model[c][0] * model[c][1] for c in MFMA_CLASSES)
+        mf = sum(model[c][0] * model[c][1] for c in MFMA_CLASSES if c in model)
     k1_cold = None if args.no_kernel_timing or s.dtype != "bf16" else cfg_euler_cold(s)
 
     res = {
@@ -346,6 +357,8 @@ def main():
                    "frames": s.n_frames, "layers": s.n_layers, "d_model": s.d_model,
                    "heads": s.n_heads, "ffn": s.ffn_dim, "latent": s.latent_dim,
                    "euler_steps": s.n_steps, "guidance": list(s.guidance), "launch": "graph" if args.graph else "eager",
+                   "block": {"cond_mode": s.cond_mode, "context_tokens": s.n_prefix if s.cond_mode == "cross" else 0,
+                             "norm": s.norm, "mlp": s.mlp, "rope": s.rope},
                    "sampler": {k: (list(v) if isinstance(v, tuple) else v) for k, v in options.items()}},
         "row_evaluations_run": row_evals, "guided_evaluations_per_request": guided_evals, "cache_hits": cache_hits,
         "latent_frame_steps_per_s": valid_frames * s.n_steps / (ms / 1e3),

@@ -465,6 +465,11 @@ __global__ void swiglu_f32_kernel(const float* gu, float* act, long long M, int 
     act[i] = silu(r[0]) * r[16];
 }
 
+__global__ void silu_bf16_kernel(const float* in, bf16* out, long long n) {
+    const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) out[i] = (bf16)silu(in[i]);
+}
+
 __global__ void expand_context_kernel(const float* cond, float* xctx, int R, int cond0, long long per_row) {
     const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
     const int row = blockIdx.y, b = row / R, r = row - b * R;
@@ -590,6 +595,11 @@ void launch_swiglu_f32(const float* gu, float* act, long long M, int f, const in
     const long long n = M * f;
     if (n <= 0) return;
     swiglu_f32_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(gu, act, M, f, n_dev);
+}
+
+void launch_silu_bf16(const float* in, bf16* out, long long n, hipStream_t s) {
+    if (n <= 0) return;
+    silu_bf16_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(in, out, n);
 }
 
 void launch_expand_context(const float* cond, float* xctx, int R, int nb, int cond0, long long per_row,

@@ -173,6 +173,8 @@ void launch_rope_f32(float* qkv, long long n_tok, int ld, int T, int d, int hd, 
                      const int32_t* n_dev, hipStream_t s);
 // act[m, 16b + i] = SiLU(gu[m, 32b + i]) * gu[m, 32b + 16 + i] (fp32, the interleaved gate-up rows).
 void launch_swiglu_f32(const float* gu, float* act, long long M, int f, const int32_t* n_dev, hipStream_t s);
+// out[i] = bf16(SiLU(in[i])).
+void launch_silu_bf16(const float* in, bf16* out, long long n, hipStream_t s);
 // Context of every branch row: xctx[b*R + r] = b >= cond0 ? cond[r] : 0 (per_row floats each).
 void launch_expand_context(const float* cond, float* xctx, int R, int nb, int cond0, long long per_row,
                            hipStream_t s);

@@ -694,9 +694,27 @@ cfm_status cfm_sample_ex(cfm_ctx* c, const float* x0, const float* cond, const f
     timed(c, CFM_K_HOISTED, s, [&] {
         launch_timestep_embedding(temb, n_eval, g.t_freq_dim, op.schedule, S, op.native, per_step, s);
     });
-    hoisted(false, temb, g.t_freq_dim, c->t1w, c->t1b, n_eval, d, g.t_freq_dim, tpre, d);
-    hoisted(true, tpre, d, c->t2w, c->t2b, n_eval, d, d, ct, d);
-    if (g.spk_dim > 0) hoisted(false, spk, g.spk_dim, c->spkw, c->spkb, R, d, g.spk_dim, spkproj, d);
+    if (bf) {
+        // bf16 sampler: the timestep MLP and the speaker projection on matrix cores
+        // (operands rounded to bf16 like every GEMM operand of that path); the SiLU
+        // between the two MLP layers writes the second layer's bf16 A operand into the
+        // condition-vector region, which is only filled after that layer
+        auto f32gemm = [&](bool a_f32, const void* A, int lda, Slot w, Slot b, int M, int K, float* o) {
+            EpiParams ep;
+            ep.bias = wp<float>(c, b);
+            ep.out = o;
+            ep.ldo = d;
+            gemm(CFM_K_HOISTED, a_f32, A, lda, w, M, d, K, EPI_F32, ep);
+        };
+        f32gemm(true, temb, g.t_freq_dim, c->t1w, c->t1b, n_eval, g.t_freq_dim, tpre);
+        timed(c, CFM_K_HOISTED, s, [&] { launch_silu_bf16(tpre, (bf16*)cvec, (long long)n_eval * d, s); });
+        f32gemm(false, cvec, d, c->t2w, c->t2b, n_eval, d, ct);
+        if (g.spk_dim > 0) f32gemm(true, spk, g.spk_dim, c->spkw, c->spkb, R, g.spk_dim, spkproj);
+    } else {
+        hoisted(false, temb, g.t_freq_dim, c->t1w, c->t1b, n_eval, d, g.t_freq_dim, tpre, d);
+        hoisted(true, tpre, d, c->t2w, c->t2b, n_eval, d, d, ct, d);
+        if (g.spk_dim > 0) hoisted(false, spk, g.spk_dim, c->spkw, c->spkb, R, d, g.spk_dim, spkproj, d);
+    }
     // the modulation vectors of every evaluation, layer and conditioning vector: one
     // GEMM over the stacked adaLN weights (bf16 sampler: silu(c) rounded to bf16 as
     // the A operand on matrix cores, like every other GEMM operand of that path)
