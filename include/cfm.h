@@ -330,8 +330,8 @@ cfm_status cfm_cfg_euler(const float* v, const float* w, int nb, float dt, const
  *   4: SwiGLU of a fused gate-up weight stored interleaved in groups of 16 rows
  *      (cfm_tensor_desc, interleave 16): C bf16 [M, N/2],
  *      C[m, 16b + i] = SiLU(acc[m, 32b + i] + bias) * (acc[m, 32b + 16 + i] + bias),
- *      N % 32 == 0 (vox-serve/VoiceHub "Custom Triton and CUDA kernels": SwiGLU;
- *      vLLM-Omni "CFM/LocDiT decode-tail batching": fused gate-up MLP).
+ *      N % 32 == 0 (VoiceHub "Custom Triton and CUDA kernels": SwiGLU; vLLM-Omni
+ *      TTS blog "CFM/LocDiT decode-tail batching": fused gate-up MLP).
  * K % 8 == 0 (bf16 A) or K % 4 == 0 (fp32 A); lda, ldw multiples of 8 (bf16)
  * or 4 (fp32 A); ldw >= K rounded up to 8 with zero padding.
  * tile: 0 = chosen from the problem size (what cfm_sample uses); 1 = 128x128
