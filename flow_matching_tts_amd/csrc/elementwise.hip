@@ -214,9 +214,19 @@ adaln_kernel(LnParams p, int tpw) {
     const int d4 = p.d >> 2;
     if (p.n_dev) p.n_out = min(p.n_out, (long long)*p.n_dev);
     if (o0 >= p.n_out) return;
+    // output token o -> its token in the row-major output order (rows of Tout), from
+    // which the input token and the modulation vectors follow
+    auto rm_of = [&](long long o) {
+        if (p.inter_nb == 0) return o;
+        const long long fr = o / p.inter_nb;
+        const int b = (int)(o - fr * p.inter_nb);
+        const long long r = fr / p.Tout;
+        return ((long long)b * p.inter_R + r) * p.Tout + (fr - r * p.Tout);
+    };
     auto src_of = [&](long long o) {
-        const long long row = o / p.Tout;
-        const int t = (int)(o - row * p.Tout);
+        const long long om = rm_of(o);
+        const long long row = om / p.Tout;
+        const int t = (int)(om - row * p.Tout);
         return (const f32x4*)(p.h + (row * p.Tin + p.off + t) * p.d);
     };
     f32x4 cur[V], nxt[V], sh[V], sc[V];
@@ -236,11 +246,11 @@ adaln_kernel(LnParams p, int tpw) {
         // modulation vectors first, the next token's row after them: the output
         // below waits only for the vectors (loads complete in issue order), so its
         // stores go out while the next row is still in flight
-        const float* shp = p.shift.at(o);
+        const float* shp = p.shift.at(rm_of(o));
         if (shp != sh_ptr) {              // wave-uniform
             sh_ptr = shp;
             const f32x4* s4 = (const f32x4*)shp;
-            const f32x4* c4 = (const f32x4*)p.scale.at(o);
+            const f32x4* c4 = (const f32x4*)p.scale.at(rm_of(o));
 #pragma unroll
             for (int i = 0; i < V; ++i) {
                 const int c = lane + i * 64;

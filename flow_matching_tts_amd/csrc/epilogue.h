@@ -169,6 +169,48 @@ __device__ __forceinline__ void epi_block(const EpiParams& p, const f32x16& acc,
         __builtin_amdgcn_wave_barrier();
         return;
     }
+    if constexpr (EPI == EPI_VOUT_EULER) {
+        // the block's 32 rows are 32 / nb frames with their nb branch rows next to each
+        // other; lane: frame (lane / 8) + 8 q of the block, columns 4 (lane % 8) .. + 3
+        const int nbv = p.nb, c0 = (lane & 7) * 4, n = nb0 + c0;
+        const long long nfr = (long long)p.R * p.Tx;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int fi = (lane >> 3) + 8 * q;
+            const long long fr = mb / nbv + fi;
+            if (fi * nbv >= 32 || fr >= nfr || n >= N) continue;
+            const bool valid = p.mask == nullptr || p.mask[fr] != 0;
+            const float* xi = p.x_in + fr * p.ldo;
+            float* xo = p.x_out + fr * p.ldo;
+            if (n + 3 < N) {
+                const f32x4 b4 = p.bias ? *(const f32x4*)(p.bias + n) : f32x4{};
+                const f32x4 xv = *(const f32x4*)(xi + n);
+                if (valid) {
+                    f32x4 acc = xv + p.cw[0] * (*(const f32x4*)(wl + (fi * nbv) * EPI_RP + c0) + b4);
+                    if (nbv > 1) acc += p.cw[1] * (*(const f32x4*)(wl + (fi * nbv + 1) * EPI_RP + c0) + b4);
+                    *(f32x4*)(xo + n) = acc;
+                } else if (xo != xi) {
+                    *(f32x4*)(xo + n) = xv;
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if (n + e >= N) continue;
+                    const float b1 = p.bias ? p.bias[n + e] : 0.0f;
+                    const float xv = xi[n + e];
+                    if (valid) {
+                        float acc = xv + p.cw[0] * (wl[(fi * nbv) * EPI_RP + c0 + e] + b1);
+                        if (nbv > 1) acc += p.cw[1] * (wl[(fi * nbv + 1) * EPI_RP + c0 + e] + b1);
+                        xo[n + e] = acc;
+                    } else if (xo != xi) {
+                        xo[n + e] = xv;
+                    }
+                }
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+        return;
+    }
     if constexpr (EPI == EPI_QKV) {
         if (nb0 >= p.d2) {
             // lane: column li, rows 16 lh .. 16 lh + 15 (consecutive sequence positions)

@@ -565,6 +565,7 @@ void launch_a(int tile, int epi, const AT* A, int lda, const bf16* W, int ldw, i
         case EPI_VOUT: launch_epi<AT, EPI_VOUT>(tile, A, lda, W, ldw, M, N, K, ep, s); break;
         case EPI_QKV: launch_epi<AT, EPI_QKV>(tile, A, lda, W, ldw, M, N, K, ep, s); break;
         case EPI_SWIGLU: launch_epi<AT, EPI_SWIGLU>(tile, A, lda, W, ldw, M, N, K, ep, s); break;
+        case EPI_VOUT_EULER: launch_epi<AT, EPI_VOUT_EULER>(tile, A, lda, W, ldw, M, N, K, ep, s); break;
         default: break;
     }
 }

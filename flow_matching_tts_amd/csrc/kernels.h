@@ -17,6 +17,9 @@ enum Epi {
     EPI_QKV = 6,       // q|k columns -> out bf16 [m, 2d]; v columns -> vt bf16 [row, head, hd, Tp] (transposed)
     EPI_SWIGLU = 7,    // fused gate-up: block of 32 columns 32b .. 32b+31 = 16 gate then 16 up columns of
                        // features 16b .. 16b+15; out bf16 [m, 16b + i] = SiLU(gate_i + bias) * (up_i + bias)
+    EPI_VOUT_EULER = 8,  // velocity rows interleaved by frame (m = frame * nb + b, nb = 1 or 2), guidance
+                         // combine and Euler step in the epilogue: x_out[frame, n] = x_in[frame, n] +
+                         // sum_b cw[b] (acc + bias) on valid frames; masked frames keep x_in
 };
 
 struct EpiParams {
@@ -49,6 +52,11 @@ struct EpiParams {
     // a long K may then split K (the library picks the split; M * N * splits floats)
     float* split_ws = nullptr;
     long long split_ws_floats = 0;
+    // EPI_VOUT_EULER: latent x [R * Tx frames, ldo] in and out (may be the same), branch
+    // weights (dt already applied), frame mask [R * Tx] or null (R, Tx, nb above)
+    const float* x_in = nullptr;
+    float* x_out = nullptr;
+    float cw[3] = {0.0f, 0.0f, 0.0f};
     // EPI_QKV, optional: rotary embedding of the q|k columns, table [T, rope_hd / 2] of
     // (cos, sin) pairs by token position t (m - row_off[tok_row[m]], or m % T)
     const float* rope = nullptr;
@@ -108,6 +116,9 @@ struct LnParams {
     int out_bf16;
     const int32_t* n_dev = nullptr;   // optional device count of output tokens (at most n_out)
     int rms = 0;                      // RMSNorm h / sqrt(mean(h^2) + 1e-6) instead of LayerNorm
+    // optional output order interleaved by frame: output token o = (r * Tout + t) * inter_nb + b
+    // holds what the row-major order puts at (b * inter_R + r) * Tout + t (0 = row-major)
+    int inter_nb = 0, inter_R = 0;
 };
 void launch_adaln(const LnParams& p, hipStream_t s);
 

@@ -773,7 +773,11 @@ cfm_status cfm_sample_ex(cfm_ctx* c, const float* x0, const float* cond, const f
     // Rows are branch-major (row = b * R + r): with nbe = 1 the single row of a
     // request is row r, and in the packed layout rows 0 .. R - 1 are a prefix of the
     // layout, whose token count is row_off[R].
-    auto estimate = [&](int j, int nbe, const float* xl) {
+    // `fuse`, when given, is the guidance combine + Euler step that follows this
+    // evaluation: where the layout allows (bf16, rows not packed, one or two branch
+    // rows, no adaptive lanes) it runs in the velocity projection's epilogue and the
+    // lambda returns true; otherwise the velocities go to `vel` and the caller combines.
+    auto estimate = [&](int j, int nbe, const float* xl, const CfgEulerArgs* fuse) -> bool {
         const int Ne = nbe * R;
         const int cond0 = nbe == 1 ? 0 : 1;
         const int spk_branch = g.spk_dim > 0 ? nbe - 1 : -1;
@@ -896,18 +900,28 @@ cfm_status cfm_sample_ex(cfm_ctx* c, const float* x0, const float* cond, const f
             if (caching && l == cb - 1)   // computed: save the residual; hit: add the saved one
                 timed(c, CFM_K_HOISTED, s, [&] { launch_cache_apply(h, resid, probe, d, tk, cstate, s); });
         }
+        const bool fused = fuse != nullptr && bf && !packed && !adaptive && nbe <= 2 && fuse->lane_off == nullptr;
         {
             const float* mf = modk + (long long)L * 6 * d;
             LnParams ln;
             ln.h = h; ln.y = act; ln.d = d; ln.n_out = (long long)Ne * Tx; ln.Tin = T; ln.Tout = Tx; ln.off = P;
             ln.shift = rowmod(mf, Tx); ln.scale = rowmod(mf + d, Tx); ln.out_bf16 = bf; ln.rms = rms;
             if (packed) { ln.n_out = NTk; ln.Tin = ln.Tout = 1; ln.n_dev = ntok; }   // tokens map one to one
+            if (fused) { ln.inter_nb = nbe; ln.inter_R = R; }   // the nbe rows of a frame next to each other
             timed(c, CFM_K_ADALN, s, [&] { launch_adaln(ln, s); });
-            EpiParams ep; ep.bias = wp<float>(c, c->outb); ep.out = vel; ep.ldo = C;
+            EpiParams ep; ep.bias = wp<float>(c, c->outb); ep.ldo = C;
             ep.R = R; ep.Tx = Tx; ep.mask = frame_mask;
-            ep.tok_row = tokrow; ep.row_off = rowoff; ep.m_dev = ntok;
-            gemm(CFM_K_GEMM_OUT, false, act, d, c->outw, packed ? (int)NTk : Ne * Tx, C, d, EPI_VOUT, ep);
+            if (fused) {
+                ep.nb = nbe; ep.x_in = fuse->x_in; ep.x_out = fuse->x_out;
+                ep.cw[0] = fuse->w0; ep.cw[1] = fuse->w1;
+                gemm(CFM_K_GEMM_OUT, false, act, d, c->outw, Ne * Tx, C, d, EPI_VOUT_EULER, ep);
+            } else {
+                ep.out = vel;
+                ep.tok_row = tokrow; ep.row_off = rowoff; ep.m_dev = ntok;
+                gemm(CFM_K_GEMM_OUT, false, act, d, c->outw, packed ? (int)NTk : Ne * Tx, C, d, EPI_VOUT, ep);
+            }
         }
+        return fused;
     };
 
     // guidance weights of a guided evaluation (weights of the branch velocities
@@ -922,13 +936,13 @@ cfm_status cfm_sample_ex(cfm_ctx* c, const float* x0, const float* cond, const f
         return true;   // full CFG; adaptive lanes are decided on the device
     };
     // x_out = x_in + dt * (guided combine of the nbe rows just evaluated)
-    auto combine = [&](int nbe, float dt, const float* xin, float* xout, const int32_t* lane_off) {
+    auto combine_args = [&](int nbe, float dt, const float* xin, float* xout, const int32_t* lane_off) {
         CfgEulerArgs a;
         a.v = vel; a.nb = nbe; a.mask = frame_mask; a.R = R; a.Tx = Tx; a.C = C;
         a.x_in = xin; a.x_out = xout; a.lane_off = lane_off; a.w_full = dt;
         if (nbe == 1) a.w0 = dt;
         else { a.w0 = dt * w[0]; a.w1 = dt * w[1]; a.w2 = dt * w[2]; }
-        timed(c, CFM_K_CFG_EULER, s, [&] { launch_cfg_euler(a, s); });
+        return a;
     };
 
     // ---- steps: the grid is rebuilt before the loop (uniform, quadratic, trailing or
@@ -954,12 +968,13 @@ cfm_status cfm_sample_ex(cfm_ctx* c, const float* x0, const float* cond, const f
             const double te = host_eval_time(op.schedule, S, op.native, per_step, j);
             const int nbe = guided_at(te) ? nb : 1;
             guided_evals += nbe > 1 ? 1 : 0;
-            estimate(j, nbe, e == 0 ? out : xmid);
+            const CfgEulerArgs a = per_step == 2 && e == 0 ? combine_args(nbe, 0.5f * dt, out, xmid, lane_off)  // half step
+                                                           : combine_args(nbe, dt, out, out, lane_off);
+            const bool fused = estimate(j, nbe, e == 0 ? out : xmid, &a);
             if (adaptive && e == 0)
                 launch_adaptive_update(vel, nb, frame_mask, R, Tx, C, st_cur, st_next, k, op.warmup, op.patience,
                                        op.threshold, per_step, s);
-            if (per_step == 2 && e == 0) combine(nbe, 0.5f * dt, out, xmid, lane_off);   // half step
-            else combine(nbe, dt, out, out, lane_off);
+            if (!fused) timed(c, CFM_K_CFG_EULER, s, [&] { launch_cfg_euler(a, s); });
         }
     }
     if (op.guided_out != nullptr) {

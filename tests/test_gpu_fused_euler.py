@@ -1,0 +1,72 @@
+"""The guidance combine + Euler step fused into the velocity projection's epilogue.
+
+On the bf16 path with unpacked rows and one or two branch rows per evaluation, the
+final norm writes the branch rows of a frame next to each other and the velocity
+GEMM's epilogue applies x <- x + dt * sum_b w_b v_b directly (VoiceHub, "Custom
+Triton and CUDA kernels": packed CFG combination plus an Euler update). Checked
+here: the fused path gives the same bits as the separate combine kernel (a batch
+with an all-ones frame mask runs the packed layout, which keeps the separate
+kernel, on identical token positions); a constant velocity field (zero output
+weights, bias b) is integrated exactly to x0 + b through the fused epilogue on
+every schedule, with the midpoint solver and with unguided evaluations; masked
+frames come back untouched.
+"""
+import numpy as np
+import pytest
+
+import synth
+from tests.helpers import config_for, dev
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import flow_matching_tts_amd as F
+    F.load()
+
+
+def _run(smp, s, I, mask=None, **opt):
+    out = smp.sample(dev(I["x0"]), dev(I["cond"]), mask=None if mask is None else dev(mask), spk=dev(I["spk"]),
+                     n_steps=s.n_steps, guidance=s.guidance, **opt)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("name", ["mel_dit", "locdit_tail"])
+def test_fused_step_equals_the_separate_combine(name):
+    import flow_matching_tts_amd as F
+    if name == "mel_dit":
+        s = synth.workload(name).replace(n_layers=2, n_frames=296, n_requests=2, n_steps=3)
+    else:
+        s = synth.workload(name).replace(n_requests=9, n_steps=3, n_layers=2)
+    W, I = synth.make_weights(s), synth.make_inputs(s)
+    smp = F.Sampler(config_for(s, max_steps=8), W)
+    fused = _run(smp, s, I)
+    if name == "mel_dit":   # all-ones mask: packed rows, separate combine kernel
+        sep = _run(smp, s, I, mask=np.ones((s.n_requests, s.n_frames), np.uint8))
+        np.testing.assert_array_equal(fused, sep)
+    # the midpoint solver runs the fused step twice per step (half step into its own buffer)
+    mid = _run(smp, s.replace(n_steps=2), I, solver="midpoint")
+    assert np.isfinite(mid).all() and np.abs(mid - I["x0"]).max() > 0
+
+
+@pytest.mark.parametrize("opt", [dict(), dict(schedule="trailing"), dict(solver="midpoint"),
+                                 dict(guidance_mode="interval", interval=(0.3, 0.6))])
+def test_constant_field_integrates_exactly_through_the_fused_step(opt):
+    """Zero output weights make v = b for every branch; any guidance combine of equal
+    branch velocities is b, so S steps reach x0 + b (sum of dt = 1) up to fp32 rounding."""
+    import flow_matching_tts_amd as F
+    s = synth.workload("mel_dit").replace(n_layers=1, n_frames=160, n_requests=3, n_steps=6)
+    W, I = synth.make_weights(s), synth.make_inputs(s)
+    W = dict(W)
+    W["final.out.weight"] = np.zeros_like(W["final.out.weight"])
+    b = synth.round_bf16(np.linspace(-2.0, 3.0, s.latent_dim).astype(np.float32))
+    W["final.out.bias"] = b
+    smp = F.Sampler(config_for(s, max_steps=2 * s.n_steps), W)
+    got = _run(smp, s, I, **opt)
+    want = I["x0"].astype(np.float64) + b
+    np.testing.assert_allclose(got, want, rtol=0, atol=16 * s.n_steps * np.finfo(np.float32).eps * 4)
