@@ -164,6 +164,46 @@ def traffic_probe():
     print(json.dumps({"probe": "copy", "bytes_read": PROBE_BYTES, "bytes_written": PROBE_BYTES}), flush=True)
 
 
+def gemm_kscan(reps: int = 10):
+    """The block GEMMs of the Mel DiT workload (16 000 tokens) through the GEMM entry point at
+    K = 256 .. 4096 with the library's own tile choice: the slope of time over K is the main
+    loop's rate, the intercept the fixed cost of a launch (prologue, epilogue, ramp)."""
+    import torch
+    import flow_matching_tts_amd as F
+    M, d, f = 16000, 1024, 2048
+    shapes = {"qkv (bf16 out)": (3 * d, 1), "proj / fc2 (gated residual)": (d, 3), "fc1 (GELU)": (f, 2)}
+    Ks = [256, 512, 1024, 2048, 4096]
+    rng = np.random.default_rng(0)
+    A = torch.from_numpy(rng.standard_normal((M, max(Ks)), dtype=np.float32)).to(torch.bfloat16).cuda()
+    res = {}
+    for name, (N, epi) in shapes.items():
+        W = torch.from_numpy(rng.standard_normal((N, max(Ks)), dtype=np.float32) * 0.02).to(torch.bfloat16).cuda()
+        bias = torch.zeros(N, dtype=torch.float32, device="cuda")
+        gate = torch.ones(N, dtype=torch.float32, device="cuda")
+        out = torch.zeros((M, N), dtype=torch.bfloat16 if epi in (1, 2) else torch.float32, device="cuda")
+        rows = []
+        for K in Ks:
+            Ak, Wk = A[:, :K].contiguous(), W[:, :K].contiguous()
+            call = lambda: F.gemm_bf16(Ak, Wk, bias, epilogue=epi, out=out, gate=gate)
+            call()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                call()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / reps
+            rows.append({"K": K, "us": us, "tflops": 2.0 * M * N * K / us / 1e6})
+        x = np.array([r["K"] for r in rows], float)
+        y = np.array([r["us"] for r in rows])
+        slope, icpt = np.polyfit(x, y, 1)
+        res[name] = {"N": N, "points": rows, "main_loop_pflops": 2.0 * M * N / slope / 1e9,
+                     "fixed_us": float(icpt)}
+        log(f"[kscan] {name}: main loop {res[name]['main_loop_pflops']:.3f} PFLOP/s, fixed {icpt:.1f} us")
+    print(json.dumps({"gemm_kscan": res, "M": M}), flush=True)
+
+
 def sources_sha256():
     import hashlib
     h = hashlib.sha256()
@@ -203,6 +243,8 @@ def main():
     ap.add_argument("--no-kernel-timing", action="store_true")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="only copy a known number of bytes (calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--gemm-kscan", action="store_true",
+                    help="only time the block GEMM shapes at several K (main-loop rate and fixed cost)")
     ap.add_argument("--graph", action="store_true",
                     help="capture one sampling call in a HIP graph and time its replays")
     ap.add_argument("--schedule", default="uniform", choices=["uniform", "quadratic", "trailing", "native"])
@@ -214,6 +256,9 @@ def main():
                     help="threshold, warm-up steps, patience")
     ap.add_argument("--cache", action="store_true", help="block-residual cache with its default settings")
     args = ap.parse_args()
+    if args.gemm_kscan:
+        gemm_kscan()
+        return
     if args.traffic_probe:
         traffic_probe()
         return

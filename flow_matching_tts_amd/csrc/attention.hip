@@ -356,6 +356,125 @@ struct KvStage {
     }
 };
 
+// Tiny sequences (at most 32 queries and 32 keys per row, the LocDiT decode tail):
+// one wave per (row, head), four heads per block, no LDS and no barrier. Every
+// operand comes straight from global memory into MFMA fragments (K rows and Q rows
+// 16 bytes per lane, V^T rows 8 bytes per lane in the key order of the P^T
+// fragments), so the wave issues all its loads at once; S^T = K Q^T is one 32x32
+// block (4 MFMAs), the softmax runs on its accumulators (one query per lane pair),
+// and O^T = V^T P^T takes 4 more MFMAs. At these sizes a launch is bound by load
+// latency, not by arithmetic.
+constexpr int TINY_T = 32;
+constexpr int TINY_W = 4;   // heads (waves) per block
+
+__global__ void __launch_bounds__(64 * TINY_W)
+attn_tiny_kernel(AttnParams p) {
+    if (p.active != nullptr && *p.active == 0) return;   // skipped (block-uniform)
+    const int row = blockIdx.y, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int head = blockIdx.x * TINY_W + wave;
+    if (head >= p.H) return;           // wave-uniform; nothing below synchronises waves
+    const int j = lane & 31, h = lane >> 5;
+    long long rbase;
+    int T;
+    if (p.row_off) {
+        rbase = p.row_off[row];
+        T = p.row_off[row + 1] - (int)rbase;
+    } else {
+        rbase = (long long)row * p.T;
+        T = p.T;
+    }
+    const int d = p.H * HD;
+    const long long ldk = 2LL * d;
+    const bf16* qbase = (const bf16*)p.qkv + rbase * ldk + head * HD;
+    const bool cross = p.kx != nullptr;
+    const int Tk = cross ? p.Tk : T;
+    const long long ldkk = cross ? p.ldkx : ldk;
+    const bf16* kbase = cross ? (const bf16*)p.kx + (long long)row * p.Tk * p.ldkx + head * HD : qbase + d;
+    const bf16* vtbase = (const bf16*)p.vt + (long long)(row * p.H + head) * HD * p.Tp;
+    const int rr = row % p.kv_mod;
+    const int kvl = min(p.kv_len[rr], Tk);
+
+    // fragments: K row j (A of S^T), Q row j (B of S^T), V^T rows dt*32 + j in the key
+    // order of the P^T fragments (slot e of k-step ss: key 16 ss + 4h + e, e < 4, or
+    // 16 ss + 8 + 4h + e - 4)
+    bf16x8 ka[4], qf[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        ka[kk] = j < Tk ? *(const bf16x8*)(kbase + (long long)j * ldkk + kk * 16 + h * 8) : bf16x8{};
+        qf[kk] = j < T ? *(const bf16x8*)(qbase + (long long)j * ldk + kk * 16 + h * 8) : bf16x8{};
+    }
+    bf16x4 vlo[2][2], vhi[2][2];
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int ss = 0; ss < 2; ++ss) {
+            const bf16* vr = vtbase + (long long)(dt * 32 + j) * p.Tp + 16 * ss + 4 * h;
+            vlo[dt][ss] = *(const bf16x4*)vr;
+            vhi[dt][ss] = *(const bf16x4*)(vr + 8);
+        }
+    // key validity: lane j's key j, gathered into one 32-bit mask
+    const bool kj = j < kvl && p.kvalid[(long long)rr * p.Tp + j] != 0;
+    const uint32_t vmask = (uint32_t)__ballot(kj);
+    auto valid = [&](int key) { return ((vmask >> key) & 1u) != 0; };
+
+    // S^T = K Q^T: s[g*4 + r] = score(key 8g + 4h + r, query j)
+    f32x16 sc = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk], qf[kk], sc, 0, 0, 0);
+    const float sl2 = 1.4426950408889634f / sqrtf((float)HD);   // 1/sqrt(hd) in base-2 units
+    float mx = -INFINITY;
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int key = 8 * g + 4 * h + r;
+            if (!valid(key)) sc[g * 4 + r] = -INFINITY;
+            mx = fmaxf(mx, sc[g * 4 + r]);
+        }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m = mx == -INFINITY ? 0.0f : mx * sl2;     // no valid key: every p is 0
+    float ls = 0.0f;
+    bf16x8 pb[2];
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float pv = __builtin_amdgcn_exp2f(fmaf(sc[g * 4 + r], sl2, -m));
+            ls += pv;
+            pb[g >> 1][(g & 1) * 4 + r] = (bf16)pv;
+        }
+    const float l = ls + __shfl_xor(ls, 32, 64);
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+
+    // O^T = V^T P^T; values of invalid keys are zeroed (their p is 0, and 0 times a
+    // non-finite value behind the padding must not reach the output)
+    f32x16 oacc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int ss = 0; ss < 2; ++ss) {
+            bf16x8 a;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                a[e] = valid(16 * ss + 4 * h + e) ? vlo[dt][ss][e] : (bf16)0.0f;
+                a[4 + e] = valid(16 * ss + 8 + 4 * h + e) ? vhi[dt][ss][e] : (bf16)0.0f;
+            }
+            oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ss], oacc[dt], 0, 0, 0);
+        }
+    if (j < T) {
+        bf16* dst = (bf16*)p.o + (rbase + j) * d + head * HD;
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                bf16x4 o4;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) o4[r] = (bf16)(oacc[dt][g * 4 + r] * inv);
+                *(bf16x4*)(dst + dt * 32 + 8 * g + 4 * h) = o4;
+            }
+    }
+}
+
 // Short sequences (one key tile, T <= 64): one wave per 32 queries, the tile
 // staged through registers into a padded LDS layout (72-element rows) in one
 // step; with a single tile there is nothing to prefetch.
@@ -610,6 +729,12 @@ bool attention_bf16_fits(long long T) {
 
 void launch_attention_bf16(const AttnParams& p, hipStream_t s) {
     if (p.rows <= 0 || p.T <= 0) return;
+    const int tq = p.row_off ? (p.T + 7) / 8 * 8 : p.T;     // largest row: packed rows round to 8
+    const int tk = p.kx ? p.Tk : tq;
+    if (tq <= TINY_T && tk <= TINY_T) {
+        attn_tiny_kernel<<<dim3((p.H + TINY_W - 1) / TINY_W, p.rows), 64 * TINY_W, 0, s>>>(p);
+        return;
+    }
     if (p.T <= 64 && (p.kx == nullptr || p.Tk <= 64)) {
         dim3 grid((p.T + 31) / 32, p.H, p.rows);
         attn_short_kernel<1><<<grid, 64, 0, s>>>(p);

@@ -155,7 +155,8 @@ def _attn_ref(qkv, H, valid):
     return o.transpose(0, 2, 1, 3).reshape(rows, T, d)
 
 
-@pytest.mark.parametrize("rows,T,H", [(3, 200, 2), (2, 1, 1), (1, 128, 4), (2, 1000, 1), (4, 65, 3), (2, 513, 2), (3, 40, 2), (2, 64, 1)])
+@pytest.mark.parametrize("rows,T,H", [(3, 200, 2), (2, 1, 1), (1, 128, 4), (2, 1000, 1), (4, 65, 3), (2, 513, 2), (3, 40, 2),
+                                      (2, 64, 1), (5, 8, 16), (3, 17, 5), (2, 32, 3), (2, 33, 2)])
 def test_attention_bf16_matches_oracle(rows, T, H):
     import flow_matching_tts_amd as F
     qkv = _attn_case(rows, T, H, rows * T + H, scale=1.5)
@@ -183,14 +184,16 @@ def test_attention_bf16_matches_oracle(rows, T, H):
     assert rel < 6e-3, rel
 
 
-def test_attention_bf16_empty_and_single_key_rows():
+@pytest.mark.parametrize("T", [150, 24])
+def test_attention_bf16_empty_and_single_key_rows(T):
     import flow_matching_tts_amd as F
-    rows, T, H = 3, 150, 2
+    rows, H = 3, 2
     qkv = _attn_case(rows, T, H, 5)
     kv_len = np.array([0, 1, T], np.int32)
     mask = np.ones((rows, T), np.uint8)
+    key = min(77, T - 3)
     mask[2] = 0
-    mask[2, 77] = 1
+    mask[2, key] = 1
     o = torch.full((rows, T, H * 64), float("nan"), dtype=torch.bfloat16, device="cuda")
     _attn_call(qkv, H, kv_len, o, mask)
     got = o.float().cpu().numpy()
@@ -198,22 +201,23 @@ def test_attention_bf16_empty_and_single_key_rows():
     d = H * 64
     v = qkv[..., 2 * d:]
     np.testing.assert_array_equal(got[1], np.broadcast_to(v[1, 0], (T, d)))    # only key 0
-    np.testing.assert_array_equal(got[2], np.broadcast_to(v[2, 77], (T, d)))   # only key 77
+    np.testing.assert_array_equal(got[2], np.broadcast_to(v[2, key], (T, d)))  # only that key
 
 
-def test_attention_bf16_masked_keys_never_leak_non_finite_values():
+@pytest.mark.parametrize("T,n", [(130, 100), (30, 19)])
+def test_attention_bf16_masked_keys_never_leak_non_finite_values(T, n):
     import flow_matching_tts_amd as F
-    rows, T, H = 2, 130, 1
+    rows, H = 2, 1
     qkv = _attn_case(rows, T, H, 9)
-    qkv[:, 100:, 64:] = np.inf          # k and v of padded keys
-    kv_len = np.array([100, 100], np.int32)
+    qkv[:, n:, 64:] = np.inf          # k and v of padded keys
+    kv_len = np.array([n, n], np.int32)
     o = torch.zeros((rows, T, 64), dtype=torch.bfloat16, device="cuda")
     _attn_call(qkv, H, kv_len, o)
     got = o.float().cpu().numpy()
-    assert np.all(np.isfinite(got[:, :100]))
-    valid = np.arange(T)[None].repeat(rows, 0) < 100
+    assert np.all(np.isfinite(got[:, :n]))
+    valid = np.arange(T)[None].repeat(rows, 0) < n
     want = _attn_ref(np.where(np.isfinite(qkv), qkv, 0), H, valid)
-    assert np.abs(got[:, :100] - want[:, :100]).max() < 0.03 * 4
+    assert np.abs(got[:, :n] - want[:, :n]).max() < 0.03 * 4
 
 
 # ---------------------------------------------------------------- adaLN LayerNorm
