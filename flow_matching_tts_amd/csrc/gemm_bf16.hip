@@ -494,10 +494,105 @@ splitk_reduce_kernel(const float* __restrict__ part, int splits, int M, int N, E
     epi_store_vec4<EPI>(ep, m, n, v);
 }
 
+// Row-wise reduction of the gated-residual epilogue fused with the next adaLN norm:
+// one block of 256 threads per row (up to 4096 columns: 4 float4 per thread), every
+// load of the row (its K-slices, bias, gate and residual) issued at once, the slices
+// summed in slice order plus bias and gated into the residual row (the arithmetic of
+// epi_store_vec4<EPI_GATED>), then the two-pass mean / variance of the updated row
+// (mean 0 for RMSNorm) and the modulated, bf16-rounded norm output. The row sums
+// follow the adaLN kernel's order exactly (per lane l of a 64-lane wave, the float4
+// chunks l, l + 64, l + 128, ... in turn, then the wave's butterfly), so the norm
+// output has the same bits as the separate adaLN kernel's.
+constexpr int LNF_V = 4;          // float4 per thread
+constexpr int LNF_SPLITS = 4;     // most K-slices the split-K path makes
+// sum over the row in the adaLN kernel's order: part[k][l] holds chunk 64 k + l's
+// contribution (k < nk); lane l of wave 0 adds its chunks in k order, the wave sums
+// the lanes, and every thread gets the result
+__device__ __forceinline__ float row_sum_adaln_order(float (*part)[64], int nk, float* out) {
+    __syncthreads();
+    if (threadIdx.x < 64) {
+        float v = 0.0f;
+        for (int k = 0; k < nk; ++k) v += part[k][threadIdx.x];
+        v = wave_sum(v);
+        if (threadIdx.x == 0) *out = v;
+    }
+    __syncthreads();
+    return *out;
+}
+__global__ void __launch_bounds__(256)
+splitk_reduce_ln_kernel(const float* __restrict__ part, int splits, int M, int N, EpiParams ep) {
+    __shared__ float rp[LNF_V * 4][64];
+    __shared__ float rsum[2];
+    const long long plane = (long long)M * N;
+    if (ep.m_dev) M = min(M, *ep.m_dev);
+    const int m = blockIdx.x, t = threadIdx.x;
+    if (m >= M) return;                              // block-uniform
+    const int n4 = N / 4;
+    // the adaLN kernel's float4 count per lane: the next power of two of ceil(n4 / 64)
+    const int q = (n4 + 63) / 64, nk = q <= 1 ? 1 : q <= 2 ? 2 : q <= 4 ? 4 : q <= 8 ? 8 : 16;
+    const float* g = ep.gate.at(m);
+    float* hrow = (float*)ep.out + (long long)m * ep.ldo;
+    f32x4 sl[LNF_V][LNF_SPLITS], hv[LNF_V], gv[LNF_V], bv[LNF_V];
+#pragma unroll
+    for (int i = 0; i < LNF_V; ++i) {
+        const int c = t + 256 * i, n = 4 * c;
+        const bool in = c < n4;
+#pragma unroll
+        for (int k = 0; k < LNF_SPLITS; ++k)
+            sl[i][k] = in && k < splits ? *(const f32x4*)(part + k * plane + (long long)m * N + n) : f32x4{};
+        hv[i] = in ? *(const f32x4*)(hrow + n) : f32x4{};
+        gv[i] = in ? *(const f32x4*)(g + n) : f32x4{};
+        bv[i] = in && ep.bias ? *(const f32x4*)(ep.bias + n) : f32x4{};
+    }
+#pragma unroll
+    for (int i = 0; i < LNF_V; ++i) {
+        const int c = t + 256 * i;
+        if (c < n4) {
+            f32x4 v = sl[i][0];
+#pragma unroll
+            for (int k = 1; k < LNF_SPLITS; ++k)
+                if (k < splits) v += sl[i][k];
+            v += bv[i];
+            hv[i] += gv[i] * v;
+            *(f32x4*)(hrow + 4 * c) = hv[i];
+        }
+        if (c / 64 < nk) rp[c / 64][c & 63] = c < n4 ? (hv[i][0] + hv[i][1]) + (hv[i][2] + hv[i][3]) : 0.0f;
+    }
+    const float mean = ep.ln_rms ? 0.0f : row_sum_adaln_order(rp, nk, &rsum[0]) / (float)N;
+#pragma unroll
+    for (int i = 0; i < LNF_V; ++i) {
+        const int c = t + 256 * i;
+        if (c / 64 < nk) {
+            float sq = 0.0f;
+            if (c < n4) {
+                const f32x4 z = hv[i] - mean;
+                sq = (z[0] * z[0] + z[1] * z[1]) + (z[2] * z[2] + z[3] * z[3]);
+            }
+            rp[c / 64][c & 63] = sq;
+        }
+    }
+    const float rstd = rsqrtf(row_sum_adaln_order(rp, nk, &rsum[1]) / (float)N + 1e-6f);
+    const float* sh = ep.ln_shift.at(m);
+    const float* sc = ep.ln_scale.at(m);
+    bf16* yrow = (bf16*)ep.ln_y + (long long)m * N;
+#pragma unroll
+    for (int i = 0; i < LNF_V; ++i) {
+        const int c = t + 256 * i;
+        if (c < n4) {
+            const int n = 4 * c;
+            const f32x4 y = (hv[i] - mean) * rstd * (*(const f32x4*)(sc + n) + 1.0f) + *(const f32x4*)(sh + n);
+            bf16x4 b;
+            b[0] = (bf16)y[0]; b[1] = (bf16)y[1]; b[2] = (bf16)y[2]; b[3] = (bf16)y[3];
+            *(bf16x4*)(yrow + n) = b;
+        }
+    }
+}
+
 // The partial products of a split-K GEMM (EPI_F32, no bias, fp32 planes in the
-// caller's split workspace), then the reduction with the real epilogue.
+// caller's split workspace), then the reduction with the real epilogue (and, for the
+// gated residual with ep.ln_y set, the next norm: returns true then).
 template <int EPI>
-void launch_splitk(const bf16* A, int lda, const bf16* W, int ldw, int M, int N, int K, const EpiParams& ep,
+bool launch_splitk(const bf16* A, int lda, const bf16* W, int ldw, int M, int N, int K, const EpiParams& ep,
                    int splits, hipStream_t s) {
     const int kchunk = (K / splits + BK64 - 1) / BK64 * BK64;
     EpiParams pe;
@@ -505,8 +600,15 @@ void launch_splitk(const bf16* A, int lda, const bf16* W, int ldw, int M, int N,
     pe.ldo = N;
     pe.m_dev = ep.m_dev;
     launch_pp64<PP128, EPI_F32>(A, lda, W, ldw, M, N, K, pe, s, splits, kchunk);
+    if constexpr (EPI == EPI_GATED) {
+        if (ep.ln_y != nullptr && N <= LNF_V * 4 * 256 && splits <= LNF_SPLITS) {
+            splitk_reduce_ln_kernel<<<M, 256, 0, s>>>(ep.split_ws, splits, M, N, ep);
+            return true;
+        }
+    }
     const long long n = (long long)M * (N / 4);
     splitk_reduce_kernel<EPI><<<(int)((n + 255) / 256), 256, 0, s>>>(ep.split_ws, splits, M, N, ep);
+    return false;
 }
 
 
@@ -517,7 +619,7 @@ using C10 = Cfg<64, 64, 64, 2, 2>;      // 4 waves, 32x32 per wave: small proble
 using CF = Cfg<128, 128, 32, 2, 2>;     // fp32 A operands
 
 template <typename AT, int EPI>
-void launch_epi(int tile, const AT* A, int lda, const bf16* W, int ldw, int M, int N, int K,
+bool launch_epi(int tile, const AT* A, int lda, const bf16* W, int ldw, int M, int N, int K,
                 const EpiParams& ep, hipStream_t s) {
     if constexpr (std::is_same<AT, float>::value) {
         launch_cfg<CF, AT, EPI>(A, lda, W, ldw, M, N, K, ep, s);
@@ -537,10 +639,8 @@ void launch_epi(int tile, const AT* A, int lda, const bf16* W, int ldw, int M, i
             // rows share the call while the batch stays in this regime.
             if (tile == 10 && (EPI == EPI_GATED || EPI == EPI_F32) && ep.split_ws != nullptr && N % 4 == 0) {
                 const int splits = (int)std::min(4, K / 512);
-                if (splits >= 2 && (long long)M * N * splits <= ep.split_ws_floats) {
-                    launch_splitk<EPI>(A, lda, W, ldw, M, N, K, ep, splits, s);
-                    return;
-                }
+                if (splits >= 2 && (long long)M * N * splits <= ep.split_ws_floats)
+                    return launch_splitk<EPI>(A, lda, W, ldw, M, N, K, ep, splits, s);
             }
         }
         switch (tile) {
@@ -551,16 +651,17 @@ void launch_epi(int tile, const AT* A, int lda, const bf16* W, int ldw, int M, i
             default: launch_cfg<C1, AT, EPI>(A, lda, W, ldw, M, N, K, ep, s); break;
         }
     }
+    return false;
 }
 
 template <typename AT>
-void launch_a(int tile, int epi, const AT* A, int lda, const bf16* W, int ldw, int M, int N, int K,
+bool launch_a(int tile, int epi, const AT* A, int lda, const bf16* W, int ldw, int M, int N, int K,
               const EpiParams& ep, hipStream_t s) {
     switch (epi) {
         case EPI_F32: launch_epi<AT, EPI_F32>(tile, A, lda, W, ldw, M, N, K, ep, s); break;
         case EPI_ACT: launch_epi<AT, EPI_ACT>(tile, A, lda, W, ldw, M, N, K, ep, s); break;
         case EPI_GELU_ACT: launch_epi<AT, EPI_GELU_ACT>(tile, A, lda, W, ldw, M, N, K, ep, s); break;
-        case EPI_GATED: launch_epi<AT, EPI_GATED>(tile, A, lda, W, ldw, M, N, K, ep, s); break;
+        case EPI_GATED: return launch_epi<AT, EPI_GATED>(tile, A, lda, W, ldw, M, N, K, ep, s);
         case EPI_INPROJ: launch_epi<AT, EPI_INPROJ>(tile, A, lda, W, ldw, M, N, K, ep, s); break;
         case EPI_VOUT: launch_epi<AT, EPI_VOUT>(tile, A, lda, W, ldw, M, N, K, ep, s); break;
         case EPI_QKV: launch_epi<AT, EPI_QKV>(tile, A, lda, W, ldw, M, N, K, ep, s); break;
@@ -568,15 +669,16 @@ void launch_a(int tile, int epi, const AT* A, int lda, const bf16* W, int ldw, i
         case EPI_VOUT_EULER: launch_epi<AT, EPI_VOUT_EULER>(tile, A, lda, W, ldw, M, N, K, ep, s); break;
         default: break;
     }
+    return false;
 }
 
 }  // namespace
 
-void launch_gemm_bf16(bool a_f32, int epi, const void* A, int lda, const bf16* W, int ldw,
+bool launch_gemm_bf16(bool a_f32, int epi, const void* A, int lda, const bf16* W, int ldw,
                       int M, int N, int K, const EpiParams& ep, hipStream_t s, int tile) {
-    if (M <= 0 || N <= 0) return;
-    if (a_f32) launch_a<float>(tile, epi, (const float*)A, lda, W, ldw, M, N, K, ep, s);
-    else launch_a<bf16>(tile, epi, (const bf16*)A, lda, W, ldw, M, N, K, ep, s);
+    if (M <= 0 || N <= 0) return false;
+    if (a_f32) return launch_a<float>(tile, epi, (const float*)A, lda, W, ldw, M, N, K, ep, s);
+    return launch_a<bf16>(tile, epi, (const bf16*)A, lda, W, ldw, M, N, K, ep, s);
 }
 
 }  // namespace cfm

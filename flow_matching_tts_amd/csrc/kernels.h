@@ -57,6 +57,13 @@ struct EpiParams {
     const float* x_in = nullptr;
     float* x_out = nullptr;
     float cw[3] = {0.0f, 0.0f, 0.0f};
+    // EPI_GATED, optional: when the GEMM runs split in K, its row-wise reduction also
+    // applies the next adaLN norm to the updated rows, ln_y bf16 [m, N] =
+    // norm(h[m]) (1 + ln_scale(m)) + ln_shift(m) (LayerNorm, or RMSNorm with ln_rms);
+    // launch_gemm_bf16 returns whether it did
+    void* ln_y = nullptr;
+    RowMod ln_shift{}, ln_scale{};
+    int ln_rms = 0;
     // EPI_QKV, optional: rotary embedding of the q|k columns, table [T, rope_hd / 2] of
     // (cos, sin) pairs by token position t (m - row_off[tok_row[m]], or m % T)
     const float* rope = nullptr;
@@ -66,7 +73,8 @@ struct EpiParams {
 // bf16 MFMA GEMM, A bf16 or f32 (rounded to bf16 while staging), W bf16 [N, K].
 // tile: 0 = pick by problem size; 1 = 128x128, 6 = 128x128 with K stage 64, 10 = 64x64,
 // 14 = 256x256 ping-pong (bf16 A only above 1)
-void launch_gemm_bf16(bool a_f32, int epi, const void* A, int lda, const bf16* W, int ldw,
+// Returns true when the epilogue also produced ep.ln_y (see EpiParams).
+bool launch_gemm_bf16(bool a_f32, int epi, const void* A, int lda, const bf16* W, int ldw,
                       int M, int N, int K, const EpiParams& ep, hipStream_t s, int tile = 0);
 // fp32 SIMT GEMM, A f32 (optionally SiLU on load), W f32 or bf16 [N, K]; EPI_ACT stores f32.
 void launch_gemm_simt(bool w_bf16, bool silu_a, int epi, const float* A, int lda, const void* W,

@@ -663,12 +663,15 @@ cfm_status cfm_sample_ex(cfm_ctx* c, const float* x0, const float* cond, const f
     int32_t* tokrow = packed ? wsp<int32_t>(c, ly.tokrow) : nullptr;
 
     // GEMM through matrix cores (bf16 sampler) or fp32 FMA (fp32 sampler)
+    // (returns whether the GEMM also produced ep.ln_y, the next norm's output)
     auto gemm = [&](int cls, bool a_f32, const void* A, int lda, Slot w, int M, int Nn, int K, int epi,
-                    const EpiParams& ep) {
+                    const EpiParams& ep) -> bool {
+        bool ln_done = false;
         timed(c, cls, s, [&] {
-            if (bf) launch_gemm_bf16(a_f32, epi, A, lda, wp<bf16>(c, w), w.ld, M, Nn, K, ep, s);
+            if (bf) ln_done = launch_gemm_bf16(a_f32, epi, A, lda, wp<bf16>(c, w), w.ld, M, Nn, K, ep, s);
             else launch_gemm_simt(false, false, epi, (const float*)A, lda, c->w + w.off, w.ld, M, Nn, K, ep, s);
         });
+        return ln_done;
     };
     // hoisted fp32-activation GEMMs against config-dtype weights
     auto hoisted = [&](bool silu_a, const float* A, int lda, Slot w, Slot b, int M, int Nn, int K,
@@ -814,6 +817,11 @@ cfm_status cfm_sample_ex(cfm_ctx* c, const float* x0, const float* cond, const f
         CacheTok tk;
         tk.cap = NTk; tk.n_dev = ntok; tk.T = T; tk.tok_row = tokrow; tk.row_off = rowoff; tk.kvalid = kvalid;
         tk.R = R; tk.Tp = Tp;
+        // the gated-residual GEMMs of small batches (split in K) may also apply the next
+        // adaLN norm in their row-wise reduction (same bits as the adaLN kernel);
+        // act_ready records that LN1 is done. Not across the cache's residual update.
+        const bool ln_fuse = bf && !cross;
+        bool act_ready = false;
         for (int l = 0; l < L; ++l) {
             if (caching && l == cf) {
                 // probe: the state after the front blocks, scored against the previous one
@@ -834,7 +842,8 @@ cfm_status cfm_sample_ex(cfm_ctx* c, const float* x0, const float* cond, const f
             ln.h = h; ln.y = act; ln.d = d; ln.n_out = NTk; ln.Tin = T; ln.Tout = T; ln.off = 0;
             ln.shift = rowmod(ml + 0 * d, T); ln.scale = rowmod(ml + 1 * d, T); ln.out_bf16 = bf;
             ln.n_dev = ntok_l; ln.rms = rms;
-            timed(c, CFM_K_ADALN, s, [&] { launch_adaln(ln, s); });
+            if (!act_ready) timed(c, CFM_K_ADALN, s, [&] { launch_adaln(ln, s); });
+            act_ready = false;
             EpiParams e1; e1.bias = wp<float>(c, W.qkvb); e1.out = big;
             if (bf) {   // q|k rows of 2d (rotated in the epilogue), v transposed per head
                 e1.ldo = 2 * d; e1.vt = vt; e1.H = H; e1.T = T; e1.Tp = Tp; e1.d2 = 2 * d;
@@ -854,7 +863,11 @@ cfm_status cfm_sample_ex(cfm_ctx* c, const float* x0, const float* cond, const f
             EpiParams e2; e2.bias = wp<float>(c, W.projb); e2.out = h; e2.ldo = d; e2.gate = rowmod(ml + 2 * d, T);
             e2.m_dev = ntok_l;
             e2.split_ws = splitk; e2.split_ws_floats = splitk_floats;
-            gemm(CFM_K_GEMM_PROJ, false, act, d, W.projw, (int)NTk, d, d, EPI_GATED, e2);
+            if (ln_fuse) {   // LN2 of this block
+                e2.ln_y = act; e2.ln_shift = rowmod(ml + 3 * d, T); e2.ln_scale = rowmod(ml + 4 * d, T);
+                e2.ln_rms = rms;
+            }
+            const bool ln2_done = gemm(CFM_K_GEMM_PROJ, false, act, d, W.projw, (int)NTk, d, d, EPI_GATED, e2);
             if (cross) {
                 // cross-attention sublayer: unmodulated norm, queries, attention over the
                 // row's context keys, ungated residual (gate vector of ones)
@@ -882,7 +895,7 @@ cfm_status cfm_sample_ex(cfm_ctx* c, const float* x0, const float* cond, const f
                 gemm(CFM_K_GEMM_XATTN, false, act, d, W.xow, (int)NTk, d, d, EPI_GATED, eo);
             }
             ln.shift = rowmod(ml + 3 * d, T); ln.scale = rowmod(ml + 4 * d, T);
-            timed(c, CFM_K_ADALN, s, [&] { launch_adaln(ln, s); });
+            if (!ln2_done) timed(c, CFM_K_ADALN, s, [&] { launch_adaln(ln, s); });
             EpiParams e3; e3.bias = wp<float>(c, W.fc1b); e3.out = big; e3.ldo = f; e3.m_dev = ntok_l;
             if (!swiglu) {
                 gemm(CFM_K_GEMM_FC1, false, act, d, W.fc1w, (int)NTk, f, d, EPI_GELU_ACT, e3);
@@ -896,7 +909,11 @@ cfm_status cfm_sample_ex(cfm_ctx* c, const float* x0, const float* cond, const f
             EpiParams e4; e4.bias = wp<float>(c, W.fc2b); e4.out = h; e4.ldo = d; e4.gate = rowmod(ml + 5 * d, T);
             e4.m_dev = ntok_l;
             e4.split_ws = splitk; e4.split_ws_floats = splitk_floats;
-            gemm(CFM_K_GEMM_FC2, false, big, f, W.fc2w, (int)NTk, d, f, EPI_GATED, e4);
+            if (ln_fuse && l + 1 < L && !(caching && l == cb - 1)) {   // LN1 of the next block
+                const float* mn = modk + (long long)(l + 1) * 6 * d;
+                e4.ln_y = act; e4.ln_shift = rowmod(mn, T); e4.ln_scale = rowmod(mn + d, T); e4.ln_rms = rms;
+            }
+            act_ready = gemm(CFM_K_GEMM_FC2, false, big, f, W.fc2w, (int)NTk, d, f, EPI_GATED, e4);
             if (caching && l == cb - 1)   // computed: save the residual; hit: add the saved one
                 timed(c, CFM_K_HOISTED, s, [&] { launch_cache_apply(h, resid, probe, d, tk, cstate, s); });
         }
