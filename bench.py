@@ -148,7 +148,7 @@ def cpu_baseline(s, W, I, max_workers: int):
 
 PROBE_BYTES = 1 << 30     # bytes read (and written) by one launch of the copy probe
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_mel_dit.txt")
-TRAFFIC_SOURCES = ["gemm_bf16.hip", "epilogue.h", "kernels.h", "common.h"]
+TRAFFIC_SOURCES = ["gemm_bf16.hip", "epilogue.h", "kernels.h", "common.h", "tile_map.h"]
 
 
 def traffic_probe():

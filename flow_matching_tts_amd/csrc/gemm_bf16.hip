@@ -22,17 +22,19 @@
 // Blocks are numbered so that the tiles one XCD runs at the same time share
 // operand rows in that XCD's L2: the hardware deals block ids round-robin to
 // the 8 XCDs, so each XCD's ids are mapped to a contiguous range of tile
-// numbers, and tiles are walked in groups of GROUP_M block-rows.
+// numbers, and tiles are walked in groups of GROUP_M block-rows; under a device
+// row count the ids follow the walk directly, spreading the working leading
+// rows over all XCDs (tile_map.h).
 #include <algorithm>
 #include <type_traits>
 
 #include "epilogue.h"
+#include "tile_map.h"
 
 namespace cfm {
 namespace {
 
 constexpr int PAD = 8;        // bf16 elements of padding per LDS row
-constexpr int GROUP_M = 4;
 
 template <int BM_, int BN_, int BK_, int WGM_, int WGN_>
 struct Cfg {
@@ -110,21 +112,6 @@ struct F32Stage {
 template <typename AT, typename C> struct AStageOf { using type = Bf16Stage<C::BM, C::CPR, C::NT, C::LDK>; };
 template <typename C> struct AStageOf<float, C> { using type = F32Stage<C::BM, C::BK, C::NT, C::LDK>; };
 
-__device__ __forceinline__ void tile_of(int bid, int nblocks, int tm, int tn, int& mt, int& nt) {
-    // XCD-major renumbering: XCD x runs the ids with id % 8 == x; give it a
-    // contiguous range of tile numbers (a bijection for any block count) ...
-    const int q = nblocks / 8, rem = nblocks % 8;
-    const int xcd = bid % 8, idx = bid / 8;
-    const int b = xcd * q + min(xcd, rem) + idx;
-    // ... then walk the tiles in groups of GROUP_M block-rows, column by column
-    const int group = GROUP_M * tn;
-    const int g = b / group, first_m = g * GROUP_M;
-    const int gm = min(tm - first_m, GROUP_M);
-    const int in = b - g * group;
-    mt = first_m + in % gm;
-    nt = in / gm;
-}
-
 template <typename C, typename AT, int EPI>
 __global__ void __launch_bounds__(C::NT)
 gemm_bf16_kernel(const AT* __restrict__ A, int lda, const bf16* __restrict__ W, int ldw,
@@ -138,7 +125,7 @@ gemm_bf16_kernel(const AT* __restrict__ A, int lda, const bf16* __restrict__ W, 
     const int li = lane & 31, lh = lane >> 5;
     const int wm = wave / C::WGN, wn = wave % C::WGN;
     int mt, nt;
-    tile_of(blockIdx.x, tm * tn, tm, tn, mt, nt);
+    tile_of(blockIdx.x, tm * tn, tm, tn, ep.m_dev != nullptr, mt, nt);
     const int m0 = mt * C::BM, n0 = nt * C::BN;
     if (ep.m_dev) {
         M = min(M, *ep.m_dev);
@@ -346,7 +333,7 @@ gemm_pp64_kernel(const bf16* __restrict__ A, int lda, const bf16* __restrict__ W
         ep.out = (float*)ep.out + (long long)slice * M * ep.ldo;
     }
     int mt, nt;
-    tile_of(bid, tm * tn, tm, tn, mt, nt);
+    tile_of(bid, tm * tn, tm, tn, ep.m_dev != nullptr, mt, nt);
     const int m0 = mt * C::BM, n0 = nt * C::BN;
     if (ep.m_dev) {
         M = min(M, *ep.m_dev);
