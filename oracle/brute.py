@@ -8,7 +8,7 @@ compared end to end on a tiny workload.
 
 Pages behind it: VoiceHub "Diffusion and flow TTS optimization" (active
 families: CFM/RF with CFG and Euler; custom kernels: adaptive-norm modulation
-and residual gating, bias-GELU, packed CFG plus Euler update; padding fully
+and residual gating, bias-GELU, the guidance combine fused with the Euler step; padding fully
 masked) and the vLLM-Omni TTS blog, "CFM/LocDiT decode-tail batching".
 
 Conventions (same readings as the vectorised oracle, restated independently):

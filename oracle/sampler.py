@@ -14,8 +14,8 @@ What is computed, and where it comes from:
     "Active families" table: conditional flow matching / rectified flow sampled
     with classifier-free guidance and Euler steps.
   * same page, "Custom Triton and CUDA kernels": the estimator's repeated ops are
-    adaptive-normalization modulation with residual gating, bias-GELU, and a
-    packed CFG combination followed by an Euler update.
+    adaptive-normalization modulation with residual gating, bias-GELU, and the
+    guidance combine of the branch velocities fused with the Euler step.
   * same page, "Semantic-preserving and approximate changes" table: padded
     frames are fully masked and trimmed; packed CFG rows must equal separate
     calls with the same guidance equation.

@@ -3,7 +3,7 @@
 On the bf16 path with unpacked rows and one or two branch rows per evaluation, the
 final norm writes the branch rows of a frame next to each other and the velocity
 GEMM's epilogue applies x <- x + dt * sum_b w_b v_b directly (VoiceHub, "Custom
-Triton and CUDA kernels": packed CFG combination plus an Euler update). Checked
+Triton and CUDA kernels": the guidance combine and the Euler step in one pass). Checked
 here: the fused path gives the same bits as the separate combine kernel (a batch
 with an all-ones frame mask runs the packed layout, which keeps the separate
 kernel, on identical token positions); a constant velocity field (zero output
