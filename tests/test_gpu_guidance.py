@@ -13,7 +13,17 @@ margin of 2% on every step that counts, so that both sides must take the same
 decisions; the per-request number of guided evaluations is then compared exactly.
 Some requests get a weakened condition (their branches then nearly agree), so
 that lanes stop at different steps: each request decides on its own.
+
+At full size (the bench configuration of the Mel DiT and variable-length
+workloads) sampled requests are compared with stored oracle outputs written by
+tests/golden/make_option_refs.py: adaptive guidance on the Mel DiT (every lane
+stops after step 6, with the metric at least 5% from the threshold on every
+counted step) and limited-interval guidance with the trailing schedule and the
+midpoint solver on the packed variable-length batch.
 """
+import hashlib
+import os
+
 import numpy as np
 import pytest
 
@@ -239,3 +249,40 @@ def test_options_are_validated_before_any_work():
         assert code in str(e.value) or "capacity" in str(e.value), (opt, str(e.value))
     torch.cuda.synchronize()
     assert torch.all(out == 7.0) and torch.equal(x0, ref)
+
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+FULL_CASES = {
+    "mel_dit_adaptive": ("mel_dit", dict(guidance_mode="adaptive", adaptive=(2.0, 4, 2))),
+    "varlen_interval_midpoint": ("varlen_masked", dict(guidance_mode="interval", interval=(0.10, 0.70),
+                                                       schedule="trailing", native_steps=64, solver="midpoint")),
+}
+
+
+@pytest.mark.parametrize("case", list(FULL_CASES))
+def test_full_size_options_match_stored_oracle(case):
+    path = os.path.join(GOLDEN, f"options_{case}.npz")
+    if not os.path.exists(path):
+        pytest.skip(f"{path} not generated")
+    z = np.load(path)
+    h = hashlib.sha256()
+    for f in ("guidance.py", "sampler.py"):
+        with open(os.path.join(os.path.dirname(GOLDEN), "..", "oracle", f), "rb") as fh:
+            h.update(fh.read())
+    assert str(z["oracle_sha256"]) == h.hexdigest(), "stale oracle reference"
+    name, opt = FULL_CASES[case]
+    s = synth.workload(name)
+    W, I = synth.make_weights(s), synth.make_inputs(s)
+    got, ge, _ = _run(s, W, I, **opt)
+    reqs, frames = list(z["requests"]), z["frames"]
+    np.testing.assert_array_equal(ge[reqs], z["guided"])
+    valid = _valid(I, s)[reqs][:, frames]
+    g = got[reqs][:, frames, :]
+    x0 = I["x0"][reqs][:, frames, :]
+    err = rel_l2(g, z["out"], valid)
+    disp = rel_l2(g - x0, z["out"] - x0, valid)
+    print(f"{case}: full size, requests {reqs}, guided {ge[reqs].tolist()}: rel-L2 {err:.3e} "
+          f"(displacement {disp:.3e})")
+    assert err <= TOL[s.dtype] and disp <= TOL[s.dtype], (err, disp)
+    assert np.all(np.isfinite(got))
+    np.testing.assert_array_equal(got[~_valid(I, s)], I["x0"][~_valid(I, s)])
