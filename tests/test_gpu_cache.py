@@ -157,6 +157,18 @@ def test_cache_on_the_prefix_layout_matches_oracle():
     _check_effect(s, W, I, got, want, smp)
 
 
+def test_cache_at_full_locdit_tail_size_matches_oracle():
+    """The LocDiT decode tail in its bench configuration (64 requests x CFG, 4 layers,
+    10 steps): the count-driven schedule (C C H H C H H C H H) on the full batch."""
+    s = synth.workload("locdit_tail")
+    W, I = synth.make_weights(s), synth.make_inputs(s)
+    got, hits, smp = _run(s, W, I, cache=COUNT_ONLY)
+    want, log = _oracle(s, W, I, **COUNT_ONLY)
+    assert hits == sum(not e["compute"] for e in log) == 6
+    _check(s, I, got, want)
+    _check_effect(s, W, I, got, want, smp)
+
+
 def test_cache_options_are_validated():
     import flow_matching_tts_amd as F
     s = _mel()
