@@ -477,9 +477,11 @@ attn_tiny_kernel(AttnParams p) {
 
 // Short sequences (one key tile, T <= 64): one wave per 32 queries, the tile
 // staged through registers into a padded LDS layout (72-element rows) in one
-// step; with a single tile there is nothing to prefetch.
+// step; with a single tile there is nothing to prefetch. The staged tile, the
+// fragments and both accumulator pairs take more than 128 registers, so the
+// kernel runs at the occupancy its registers allow (no waves-per-SIMD target).
 template <int NW>
-__global__ void __launch_bounds__(64 * NW, 4)   // 4 waves per SIMD
+__global__ void __launch_bounds__(64 * NW, 1)
 attn_short_kernel(AttnParams p) {
     constexpr int QT = 32 * NW;    // queries per block
     constexpr int NT = 64 * NW;
